@@ -1,0 +1,261 @@
+"""CPU oracle for exact scaled-dot-product attention -- TEST INFRASTRUCTURE.
+
+Only the tests, the smoke check and the CPU-baseline leg of the benchmark may
+import this module. The product path (the HIP library and its binding) never
+calls it, shares no code with it, and fails loudly when its own extension is
+missing instead of falling back here.
+
+Everything is computed in float64 with numpy from whatever inputs are passed
+(the callers hand in exactly the bf16/fp16/fp32-rounded values the GPU
+receives, upcast without loss).
+
+Sources (the pages this restates in code; cited by key below):
+  [FA-mem]       "FlashAttention：优化大模型训练的内存与计算效率"
+                 (cnnetsun.cn/a/3461300) -- tutorial on the memory hierarchy,
+                 safe softmax, causal masking and debugging.
+  [FA-principle] "FlashAttention原理：从原始Attention到FlashAttention"
+                 (blog.csdn.net/qq_43527718/article/details/142302113) --
+                 standard attention, tiling, blockwise softmax, FA2 changes,
+                 and an embedded answer "写一个flashattention算子" whose numbered
+                 steps give the online-softmax update formulas.
+
+Readings taken where the pages are silent (each also listed in the design doc):
+  * scale: the scores are multiplied by ``scale`` (1/sqrt(d) in every
+    workload, as in the answer's step 3, which divides by sqrt(d)); the
+    softmax runs over the scaled scores.
+  * causal: key j is hidden from query i when j > i (square self-attention;
+    the pages only name an ``is_causal`` switch). Hidden scores are excluded
+    exactly (probability 0), not replaced by a large finite number.
+  * what is stored for the backward pass: one float per query row,
+    LSE_i = m_i + ln(l_i) -- natural log of the sum of exponentials of the
+    scaled scores (the pages say "the softmax normalization factor").
+  * the backward formulas are not on the pages; they are the derivatives of
+    the definition (chain rule through softmax), written out below.
+  * in the blockwise recurrence, a row that sees no key inside one block
+    contributes nothing from that block (its block max is -inf, its block sum 0).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "attention_forward",
+    "attention_probabilities",
+    "attention_backward",
+    "attention_forward_blockwise",
+    "merge_partials",
+]
+
+# Rows of S processed at once; bounds the float64 score chunk to
+# ROW_CHUNK * N * 8 bytes (16384 keys -> 256 MiB at 2048 rows).
+ROW_CHUNK = 2048
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def _visible(q_pos: np.ndarray, n_keys: int, causal: bool) -> np.ndarray | None:
+    """Boolean [rows, n_keys] mask of keys each query may attend to (None = all).
+
+    Causal reading: query at absolute position i sees keys 0..i.
+    """
+    if not causal:
+        return None
+    return np.arange(n_keys)[None, :] <= q_pos[:, None]
+
+
+def _scores(qc: np.ndarray, k: np.ndarray, scale: float, vis) -> np.ndarray:
+    """S = scale * Q K^T for one chunk of query rows, hidden keys set to -inf.
+
+    [FA-principle §二.2]: the standard pipeline forms S from Q and K^T; the
+    answer's step 3 divides the product by sqrt(d) (our ``scale``).
+    """
+    s = scale * (qc @ k.T)
+    if vis is not None:
+        s = np.where(vis, s, -np.inf)
+    return s
+
+
+def _head_forward(q, k, v, scale, causal, q_pos):
+    """Three-pass safe softmax attention for one head.
+
+    Pass 1: row max m of the scaled scores.     [FA-mem §2.2 safe softmax]
+    Pass 2: row sum l of exp(S - m).
+    Pass 3: P = exp(S - m) / l, O = P V, LSE = m + ln l.
+    This is the plain (unfused) definition of [FA-principle §二.2]: the
+    scores and probabilities are formed in full for a chunk of rows.
+    """
+    n_rows = q.shape[0]
+    o = np.empty((n_rows, v.shape[1]), dtype=np.float64)
+    lse = np.empty(n_rows, dtype=np.float64)
+    for r0 in range(0, n_rows, ROW_CHUNK):
+        r1 = min(r0 + ROW_CHUNK, n_rows)
+        vis = _visible(q_pos[r0:r1], k.shape[0], causal)
+        s = _scores(q[r0:r1], k, scale, vis)
+        m = s.max(axis=1, keepdims=True)                 # pass 1
+        e = np.exp(s - m)
+        l = e.sum(axis=1, keepdims=True)                 # pass 2
+        p = e / l                                        # pass 3
+        o[r0:r1] = p @ v
+        lse[r0:r1] = (m + np.log(l))[:, 0]
+    return o, lse
+
+
+def _batched(fn, arrays, n_out):
+    """Apply a per-head function over all leading (batch, head) dims."""
+    lead = arrays[0].shape[:-2]
+    flat = [a.reshape((-1,) + a.shape[-2:]) for a in arrays]
+    outs = [[] for _ in range(n_out)]
+    for i in range(flat[0].shape[0]):
+        res = fn(*[a[i] for a in flat])
+        for j in range(n_out):
+            outs[j].append(res[j])
+    return [np.stack(o).reshape(lead + o[0].shape) for o in outs]
+
+
+def attention_forward(q, k, v, scale: float, causal: bool, q_positions=None):
+    """O = softmax(scale * Q K^T [causal-masked]) V and the per-row LSE.
+
+    Shapes: q [..., Nq, d], k [..., Nk, d], v [..., Nk, dv] (leading dims are
+    batch and heads). ``q_positions`` gives the absolute position of each query
+    row for the causal mask (default 0..Nq-1), which lets a caller evaluate a
+    sampled subset of rows of a long sequence exactly.
+
+    Returns (O [..., Nq, dv], LSE [..., Nq]), float64.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    pos = np.arange(q.shape[-2]) if q_positions is None else np.asarray(q_positions)
+    if pos.shape != (q.shape[-2],):
+        raise ValueError("q_positions must have one entry per query row")
+    return tuple(_batched(lambda a, b, c: _head_forward(a, b, c, scale, causal, pos),
+                          [q, k, v], 2))
+
+
+def attention_probabilities(q, k, scale: float, causal: bool):
+    """P = softmax(scale * Q K^T) materialized ([..., N, N]; tests only)."""
+    q, k = _f64(q), _f64(k)
+    pos = np.arange(q.shape[-2])
+
+    def one(a, b):
+        s = _scores(a, b, scale, _visible(pos, b.shape[0], causal))
+        e = np.exp(s - s.max(axis=1, keepdims=True))
+        return (e / e.sum(axis=1, keepdims=True),)
+
+    return _batched(one, [q, k], 1)[0]
+
+
+def _head_backward(q, k, v, do, scale, causal):
+    """Gradients of sum(dO * O) for one head, from the definition.
+
+    Not on the pages (the answer's step 6 only says the scores are recomputed
+    instead of stored). With P the softmax of the scaled scores:
+      dV = P^T dO
+      dP = dO V^T
+      D_i = sum_j P_ij dP_ij               (softmax Jacobian-vector term)
+      dS = P * (dP - D)                    (gradient w.r.t. the scaled scores)
+      dQ = scale * dS K,   dK = scale * dS^T Q
+    P is recomputed here from Q and K (three-pass) rather than read back.
+    """
+    n = q.shape[0]
+    pos = np.arange(n)
+    dq = np.empty_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dsum = np.empty(n)
+    for r0 in range(0, n, ROW_CHUNK):
+        r1 = min(r0 + ROW_CHUNK, n)
+        s = _scores(q[r0:r1], k, scale, _visible(pos[r0:r1], k.shape[0], causal))
+        e = np.exp(s - s.max(axis=1, keepdims=True))
+        p = e / e.sum(axis=1, keepdims=True)
+        dv += p.T @ do[r0:r1]
+        dp = do[r0:r1] @ v.T
+        d_i = (p * dp).sum(axis=1, keepdims=True)
+        ds = p * (dp - d_i)
+        dq[r0:r1] = scale * (ds @ k)
+        dk += scale * (ds.T @ q[r0:r1])
+        dsum[r0:r1] = d_i[:, 0]
+    return dq, dk, dv, dsum
+
+
+def attention_backward(q, k, v, do, scale: float, causal: bool):
+    """(dQ, dK, dV, D) for the loss sum(dO * O), all float64.
+
+    D is the per-row term sum_j P_ij dP_ij (returned so tests can check that it
+    equals rowsum(dO * O)).
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    return tuple(_batched(lambda a, b, c, g: _head_backward(a, b, c, g, scale, causal),
+                          [q, k, v, do], 4))
+
+
+def _head_blockwise(q, k, v, scale, causal, block_q, block_k):
+    """One-pass blockwise attention with the online-softmax recurrence.
+
+    Loop order: query blocks outer, key/value blocks inner ([FA-principle §二.7],
+    the second FA2 change). Blocks lying entirely in the hidden upper triangle
+    are skipped ([FA-principle §二.7], third change). Per block, following the
+    answer "写一个flashattention算子" step 4 (online softmax) and step 5
+    (incremental output update), in its notation:
+      m_ij = rowmax(S_ij); p_ij = exp(S_ij - m_ij); l_ij = rowsum(p_ij)
+      m_new = max(m_prev, m_ij)
+      l_new = exp(m_prev - m_new) l_prev + exp(m_ij - m_new) l_ij
+      O_i   = (exp(m_prev - m_new) l_prev O_prev + exp(m_ij - m_new) p_ij V_j) / l_new
+    """
+    n, nk = q.shape[0], k.shape[0]
+    o = np.zeros((n, v.shape[1]))
+    lse = np.empty(n)
+    for i0 in range(0, n, block_q):
+        i1 = min(i0 + block_q, n)
+        qi = q[i0:i1]
+        m_prev = np.full((i1 - i0, 1), -np.inf)
+        l_prev = np.zeros((i1 - i0, 1))
+        o_prev = np.zeros((i1 - i0, v.shape[1]))
+        for j0 in range(0, nk, block_k):
+            j1 = min(j0 + block_k, nk)
+            if causal and j0 > i1 - 1:
+                continue                       # block fully above the diagonal
+            vis = None
+            if causal:
+                vis = np.arange(j0, j1)[None, :] <= np.arange(i0, i1)[:, None]
+            s_ij = scale * (qi @ k[j0:j1].T)
+            if vis is not None:
+                s_ij = np.where(vis, s_ij, -np.inf)
+            m_ij = s_ij.max(axis=1, keepdims=True)
+            seen = np.isfinite(m_ij)           # rows with >= 1 visible key here
+            p_ij = np.where(seen, np.exp(s_ij - np.where(seen, m_ij, 0.0)), 0.0)
+            l_ij = p_ij.sum(axis=1, keepdims=True)
+            m_new = np.maximum(m_prev, m_ij)
+            a_prev = np.where(np.isfinite(m_prev), np.exp(m_prev - m_new), 0.0)
+            a_ij = np.where(seen, np.exp(m_ij - m_new), 0.0)
+            l_new = a_prev * l_prev + a_ij * l_ij
+            o_prev = (a_prev * l_prev * o_prev + a_ij * (p_ij @ v[j0:j1])) / l_new
+            m_prev, l_prev = m_new, l_new
+        o[i0:i1] = o_prev
+        lse[i0:i1] = (m_prev + np.log(l_prev))[:, 0]
+    return o, lse
+
+
+def attention_forward_blockwise(q, k, v, scale: float, causal: bool,
+                                block_q: int = 64, block_k: int = 64):
+    """Blockwise (tiled, online-softmax) attention; equals attention_forward."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    return tuple(_batched(lambda a, b, c: _head_blockwise(a, b, c, scale, causal,
+                                                          block_q, block_k),
+                          [q, k, v], 2))
+
+
+def merge_partials(o_a, lse_a, o_b, lse_b):
+    """Combine attention computed over two disjoint key sets.
+
+    Each part is normalized over its own keys and carries its LSE; the total
+    normalizer is the log-sum of both, and each part is reweighted by
+    exp(LSE_part - LSE_total). This is the step-5 correction of the answer
+    "写一个flashattention算子" applied to two finished partial results.
+    """
+    o_a, lse_a, o_b, lse_b = _f64(o_a), _f64(lse_a), _f64(o_b), _f64(lse_b)
+    lse = np.logaddexp(lse_a, lse_b)
+    w_a = np.exp(lse_a - lse)[..., None]
+    w_b = np.exp(lse_b - lse)[..., None]
+    return w_a * o_a + w_b * o_b, lse

@@ -1,0 +1,293 @@
+"""Pins for the CPU oracle: checks against facts fixed outside the oracle.
+
+Every check here compares the oracle with something it does not compute
+itself: hand-derived worked examples (tests/golden), closed forms, invariants
+of softmax attention, pure-Python brute force on tiny inputs, finite
+differences, and an independent library routine (torch's CPU float64
+attention and autograd). test_oracle_mutations.py plants plausible mistakes in
+a copy of the oracle and shows that these pins catch them.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import (attention_backward, attention_forward, attention_forward_blockwise,
+                    attention_probabilities, merge_partials)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+# --------------------------------------------------------------- worked examples
+def test_golden_forward_hand_example():
+    fx = json.load(open(os.path.join(GOLDEN, "hand_forward_n3_d2.json")))
+    k, v = np.array(fx["k"]), np.array(fx["v"])
+    for case in fx["cases"]:
+        o, lse = attention_forward(np.array(case["q"]), k, v, case["scale"], case["causal"])
+        np.testing.assert_allclose(o, case["o"], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, case["lse"], rtol=0, atol=1e-12)
+
+
+def test_golden_backward_hand_example():
+    fx = json.load(open(os.path.join(GOLDEN, "hand_backward_n2_d1.json")))
+    q, k, v, do = (np.array(fx[n]) for n in ("q", "k", "v", "do"))
+    for case in fx["cases"]:
+        o, lse = attention_forward(q, k, v, fx["scale"], case["causal"])
+        np.testing.assert_allclose(o, case["o"], atol=1e-12)
+        np.testing.assert_allclose(lse, case["lse"], atol=1e-12)
+        dq, dk, dv, _ = attention_backward(q, k, v, do, fx["scale"], case["causal"])
+        np.testing.assert_allclose(dq, case["dq"], atol=1e-12)
+        np.testing.assert_allclose(dk, case["dk"], atol=1e-12)
+        np.testing.assert_allclose(dv, case["dv"], atol=1e-12)
+
+
+# --------------------------------------------------------------- brute force
+def brute_force(q, k, v, scale, causal):
+    """Pure-Python loops, no BLAS, no max subtraction (inputs are tiny)."""
+    n, d = len(q), len(q[0])
+    dv = len(v[0])
+    o = [[0.0] * dv for _ in range(n)]
+    lse = [0.0] * n
+    for i in range(n):
+        w = []
+        for j in range(len(k)):
+            if causal and j > i:
+                w.append(0.0)
+                continue
+            dot = 0.0
+            for c in range(d):
+                dot += q[i][c] * k[j][c]
+            w.append(math.exp(scale * dot))
+        z = sum(w)
+        lse[i] = math.log(z)
+        for c in range(dv):
+            o[i][c] = sum(w[j] * v[j][c] for j in range(len(k))) / z
+    return np.array(o), np.array(lse)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("d", [1, 2, 4])
+@pytest.mark.parametrize("causal", [False, True])
+def test_brute_force_tiny(n, d, causal):
+    seed = 100 * n + 10 * d + causal
+    q, k, v = rand((n, d), seed), rand((n, d), seed + 1), rand((n, d + 1), seed + 2)
+    scale = 0.37 + 0.1 * d
+    o, lse = attention_forward(q, k, v, scale, causal)
+    bo, blse = brute_force(q.tolist(), k.tolist(), v.tolist(), scale, causal)
+    np.testing.assert_allclose(o, bo, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, blse, rtol=0, atol=1e-12)
+
+
+def test_rectangular_and_batched_shapes():
+    q, k, v = rand((2, 3, 5, 4), 1), rand((2, 3, 7, 4), 2), rand((2, 3, 7, 6), 3)
+    o, lse = attention_forward(q, k, v, 0.5, False)
+    assert o.shape == (2, 3, 5, 6) and lse.shape == (2, 3, 5)
+    for b in range(2):
+        for h in range(3):
+            bo, blse = brute_force(q[b, h].tolist(), k[b, h].tolist(), v[b, h].tolist(),
+                                   0.5, False)
+            np.testing.assert_allclose(o[b, h], bo, atol=1e-12)
+            np.testing.assert_allclose(lse[b, h], blse, atol=1e-12)
+
+
+# --------------------------------------------------------------- closed forms
+@pytest.mark.parametrize("causal", [False, True])
+def test_rows_of_p_sum_to_one(causal):
+    p = attention_probabilities(rand((2, 64, 16), 5), rand((2, 64, 16), 6), 0.25, causal)
+    np.testing.assert_allclose(p.sum(-1), 1.0, atol=1e-12)
+    assert (p >= 0).all()
+    if causal:
+        assert np.all(np.triu(p[0], 1) == 0.0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_identical_keys_give_mean_of_v(causal):
+    n, d = 40, 8
+    q, v = rand((n, d), 7), rand((n, 3), 8)
+    krow = rand((d,), 9)
+    k = np.tile(krow, (n, 1))
+    scale = 0.3
+    o, lse = attention_forward(q, k, v, scale, causal)
+    counts = np.arange(1, n + 1) if causal else np.full(n, n)
+    mean = np.cumsum(v, 0) / counts[:, None] if causal else np.tile(v.mean(0), (n, 1))
+    np.testing.assert_allclose(o, mean, atol=1e-12)
+    np.testing.assert_allclose(lse, scale * q @ krow + np.log(counts), atol=1e-12)
+
+
+def test_causal_row0_returns_v0():
+    q, k, v = rand((1, 2, 33, 16), 10), rand((1, 2, 33, 16), 11), rand((1, 2, 33, 16), 12)
+    o, lse = attention_forward(q, k, v, 0.25, True)
+    np.testing.assert_allclose(o[..., 0, :], v[..., 0, :], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse[..., 0], 0.25 * (q[..., 0, :] * k[..., 0, :]).sum(-1),
+                               atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_scale_zero_is_uniform_average(causal):
+    n = 25
+    q, k, v = rand((n, 4), 13), rand((n, 4), 14), rand((n, 5), 15)
+    o, lse = attention_forward(q, k, v, 0.0, causal)
+    counts = np.arange(1, n + 1) if causal else np.full(n, n)
+    ref = np.cumsum(v, 0) / counts[:, None] if causal else np.tile(v.mean(0), (n, 1))
+    np.testing.assert_allclose(o, ref, atol=1e-12)
+    np.testing.assert_allclose(lse, np.log(counts), atol=1e-12)
+
+
+def test_single_key():
+    q, k, v = rand((3, 1, 1, 6), 16), rand((3, 1, 1, 6), 17), rand((3, 1, 1, 6), 18)
+    for causal in (False, True):
+        o, lse = attention_forward(q, k, v, 0.7, causal)
+        np.testing.assert_allclose(o, v, atol=1e-14)
+        np.testing.assert_allclose(lse, 0.7 * (q * k).sum(-1), atol=1e-14)
+
+
+def test_one_hot_dominant_score_selects_row():
+    n = d = 64
+    q, k, v = np.eye(n), 30.0 * np.eye(n), rand((n, d), 19)
+    o, _ = attention_forward(q, k, v, 1.0, False)
+    bound = 2 * (n - 1) * math.exp(-30) * np.abs(v).max()
+    assert np.abs(o - v).max() <= bound
+
+
+# --------------------------------------------------------------- invariants
+def test_key_permutation_invariance_and_query_equivariance():
+    q, k, v = rand((20, 8), 20), rand((30, 8), 21), rand((30, 5), 22)
+    o, lse = attention_forward(q, k, v, 0.4, False)
+    pk = np.random.default_rng(0).permutation(30)
+    o2, lse2 = attention_forward(q, k[pk], v[pk], 0.4, False)
+    np.testing.assert_allclose(o2, o, atol=1e-12)
+    np.testing.assert_allclose(lse2, lse, atol=1e-12)
+    pq = np.random.default_rng(1).permutation(20)
+    o3, lse3 = attention_forward(q[pq], k, v, 0.4, False)
+    np.testing.assert_allclose(o3, o[pq], atol=1e-12)
+    np.testing.assert_allclose(lse3, lse[pq], atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_shift_and_value_affinity(causal):
+    """K + 1u^T shifts row i's scores by scale*q_i.u (softmax unchanged);
+    O is affine in V: V W + 1c^T -> O W + 1c^T."""
+    n, d = 24, 6
+    q, k, v = rand((n, d), 23), rand((n, d), 24), rand((n, 4), 25)
+    u, w, c = rand((d,), 26), rand((4, 3), 27), rand((3,), 28)
+    o, lse = attention_forward(q, k, v, 0.5, causal)
+    o2, lse2 = attention_forward(q, k + u, v, 0.5, causal)
+    np.testing.assert_allclose(o2, o, atol=1e-12)
+    np.testing.assert_allclose(lse2, lse + 0.5 * q @ u, atol=1e-12)
+    o3, _ = attention_forward(q, k, v @ w + c, 0.5, causal)
+    np.testing.assert_allclose(o3, o @ w + c, atol=1e-12)
+
+
+def test_sampled_rows_match_full():
+    q, k, v = rand((1, 1, 300, 8), 29), rand((1, 1, 300, 8), 30), rand((1, 1, 300, 8), 31)
+    o, lse = attention_forward(q, k, v, 0.35, True)
+    rows = np.array([0, 1, 77, 150, 299])
+    os_, ls_ = attention_forward(q[..., rows, :], k, v, 0.35, True, q_positions=rows)
+    np.testing.assert_allclose(os_, o[..., rows, :], atol=1e-13)
+    np.testing.assert_allclose(ls_, lse[..., rows], atol=1e-13)
+
+
+def test_row_chunking_is_invisible(monkeypatch):
+    import oracle.attention as oa
+    q, k, v = rand((1, 2, 130, 8), 32), rand((1, 2, 130, 8), 33), rand((1, 2, 130, 8), 34)
+    do = rand((1, 2, 130, 8), 35)
+    ref_f = attention_forward(q, k, v, 0.3, True)
+    ref_b = attention_backward(q, k, v, do, 0.3, True)
+    monkeypatch.setattr(oa, "ROW_CHUNK", 7)
+    for a, b in zip(attention_forward(q, k, v, 0.3, True), ref_f):
+        np.testing.assert_allclose(a, b, atol=1e-13)
+    for a, b in zip(attention_backward(q, k, v, do, 0.3, True), ref_b):
+        np.testing.assert_allclose(a, b, atol=1e-12)
+
+
+# --------------------------------------------------------------- online recurrence
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("bq,bk", [(1, 1), (7, 5), (16, 64), (64, 16), (100, 100), (33, 17)])
+def test_blockwise_online_softmax_equals_full(causal, bq, bk):
+    q, k, v = rand((2, 97, 12), 40), rand((2, 97, 12), 41), rand((2, 97, 12), 42)
+    o, lse = attention_forward(q, k, v, 0.29, causal)
+    ob, lseb = attention_forward_blockwise(q, k, v, 0.29, causal, bq, bk)
+    np.testing.assert_allclose(ob, o, atol=1e-12)
+    np.testing.assert_allclose(lseb, lse, atol=1e-12)
+
+
+def test_two_shard_merge_equals_full():
+    q, k, v = rand((3, 50, 8), 43), rand((3, 90, 8), 44), rand((3, 90, 8), 45)
+    o, lse = attention_forward(q, k, v, 0.6, False)
+    split = np.random.default_rng(3).permutation(90)
+    a, b = split[:31], split[31:]
+    oa, la = attention_forward(q, k[:, a], v[:, a], 0.6, False)
+    ob, lb = attention_forward(q, k[:, b], v[:, b], 0.6, False)
+    om, lm = merge_partials(oa, la, ob, lb)
+    np.testing.assert_allclose(om, o, atol=1e-12)
+    np.testing.assert_allclose(lm, lse, atol=1e-12)
+
+
+# --------------------------------------------------------------- gradients
+@pytest.mark.parametrize("causal", [False, True])
+def test_gradients_match_finite_differences(causal):
+    n, d = 6, 3
+    q, k, v, do = (rand((n, d), 50 + i) for i in range(4))
+    scale = 0.8
+    dq, dk, dv, _ = attention_backward(q, k, v, do, scale, causal)
+
+    def loss(qq, kk, vv):
+        return float((attention_forward(qq, kk, vv, scale, causal)[0] * do).sum())
+
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = dict(args_p)
+            args_p[name], args_m[name] = xp, xm
+            fd[idx] = (loss(args_p["q"], args_p["k"], args_p["v"])
+                       - loss(args_m["q"], args_m["k"], args_m["v"])) / (2 * h)
+        np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gradient_invariants(causal):
+    q, k, v, do = (rand((2, 70, 8), 60 + i) for i in range(4))
+    o, _ = attention_forward(q, k, v, 0.35, causal)
+    dq, dk, dv, dsum = attention_backward(q, k, v, do, 0.35, causal)
+    # D_i = sum_j P_ij dP_ij equals rowsum(dO * O) (= dO_i . sum_j P_ij V_j).
+    np.testing.assert_allclose(dsum, (do * o).sum(-1), rtol=1e-12, atol=1e-12)
+    # Each row of dS sums to zero, so the key gradients sum to zero.
+    np.testing.assert_allclose(dk.sum(-2), 0.0, atol=1e-12)
+    # Rows of P sum to one, so the value gradients sum to the output gradients.
+    np.testing.assert_allclose(dv.sum(-2), do.sum(-2), atol=1e-12)
+
+
+# --------------------------------------------------------------- library routine
+@pytest.mark.parametrize("causal", [False, True])
+def test_matches_torch_cpu_float64_attention_and_autograd(causal):
+    shape = (2, 3, 45, 16)
+    q, k, v, do = (rand(shape, 70 + i) for i in range(4))
+    scale = 0.21
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal,
+                                                           scale=scale)
+    to.backward(torch.tensor(do))
+    o, lse = attention_forward(q, k, v, scale, causal)
+    np.testing.assert_allclose(o, to.detach().numpy(), atol=1e-12)
+    tlse = torch.logsumexp(
+        (scale * tq @ tk.transpose(-1, -2)).masked_fill(
+            torch.ones(45, 45, dtype=torch.bool).triu(1) if causal
+            else torch.zeros(45, 45, dtype=torch.bool), float("-inf")), dim=-1)
+    np.testing.assert_allclose(lse, tlse.detach().numpy(), atol=1e-12)
+    dq, dk, dv, _ = attention_backward(q, k, v, do, scale, causal)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-11)

@@ -1,0 +1,101 @@
+"""Plant plausible mistakes in a copy of the oracle; the pins must catch each.
+
+Each mutation edits one expression of oracle/attention.py's source text (a
+dropped term, a wrong sign, a wrong index or axis, a transposed operand),
+executes the edited copy as a throwaway module on the CPU, points the pin
+tests of test_oracle.py at it, and asserts that at least one pin fails.
+The real oracle is never modified.
+"""
+
+import os
+import types
+
+import pytest
+
+import test_oracle as T
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "oracle", "attention.py")
+
+MUTATIONS = [
+    ("scale dropped from scores", "s = scale * (qc @ k.T)", "s = (qc @ k.T)"),
+    ("causal direction flipped", "<= q_pos[:, None]", ">= q_pos[:, None]"),
+    ("causal hides the diagonal", "<= q_pos[:, None]", "< q_pos[:, None]"),
+    ("max over the wrong axis", "m = s.max(axis=1, keepdims=True)",
+     "m = s.max(axis=0, keepdims=True)"),
+    ("LSE without the max", "lse[r0:r1] = (m + np.log(l))[:, 0]",
+     "lse[r0:r1] = (np.log(l))[:, 0]"),
+    ("LSE without the log", "lse[r0:r1] = (m + np.log(l))[:, 0]",
+     "lse[r0:r1] = (m + l)[:, 0]"),
+    ("unnormalized output", "o[r0:r1] = p @ v", "o[r0:r1] = e @ v"),
+    ("backward drops the D term", "ds = p * (dp - d_i)", "ds = p * dp"),
+    ("backward sign flipped", "ds = p * (dp - d_i)", "ds = p * (d_i - dp)"),
+    ("dK without scale", "dk += scale * (ds.T @ q[r0:r1])", "dk += (ds.T @ q[r0:r1])"),
+    ("dQ without scale", "dq[r0:r1] = scale * (ds @ k)", "dq[r0:r1] = (ds @ k)"),
+    ("dV with P not transposed", "dv += p.T @ do[r0:r1]", "dv += p @ do[r0:r1]"),
+    ("dP uses K in place of V", "dp = do[r0:r1] @ v.T", "dp = do[r0:r1] @ k.T"),
+    ("recurrence drops the old sum", "l_new = a_prev * l_prev + a_ij * l_ij",
+     "l_new = l_prev + a_ij * l_ij"),
+    ("recurrence skips needed blocks", "if causal and j0 > i1 - 1:",
+     "if causal and j0 > i0:"),
+    ("recurrence forgets old output", "o_prev = (a_prev * l_prev * o_prev + a_ij",
+     "o_prev = (a_prev * o_prev + a_ij"),
+    ("merge weight inverted", "w_a = np.exp(lse_a - lse)[..., None]",
+     "w_a = np.exp(lse - lse_a)[..., None]"),
+]
+
+ORACLE_NAMES = ["attention_forward", "attention_backward", "attention_forward_blockwise",
+                "attention_probabilities", "merge_partials"]
+
+# (pin function, kwargs) -- the parametrized pins of test_oracle.py, one set each.
+PINS = [
+    (T.test_golden_forward_hand_example, {}),
+    (T.test_golden_backward_hand_example, {}),
+    (T.test_brute_force_tiny, dict(n=5, d=2, causal=False)),
+    (T.test_brute_force_tiny, dict(n=5, d=2, causal=True)),
+    (T.test_rectangular_and_batched_shapes, {}),
+    (T.test_rows_of_p_sum_to_one, dict(causal=True)),
+    (T.test_identical_keys_give_mean_of_v, dict(causal=True)),
+    (T.test_causal_row0_returns_v0, {}),
+    (T.test_scale_zero_is_uniform_average, dict(causal=False)),
+    (T.test_single_key, {}),
+    (T.test_one_hot_dominant_score_selects_row, {}),
+    (T.test_key_permutation_invariance_and_query_equivariance, {}),
+    (T.test_key_shift_and_value_affinity, dict(causal=False)),
+    (T.test_blockwise_online_softmax_equals_full, dict(causal=True, bq=7, bk=5)),
+    (T.test_blockwise_online_softmax_equals_full, dict(causal=False, bq=16, bk=64)),
+    (T.test_two_shard_merge_equals_full, {}),
+    (T.test_gradients_match_finite_differences, dict(causal=False)),
+    (T.test_gradient_invariants, dict(causal=True)),
+    (T.test_matches_torch_cpu_float64_attention_and_autograd, dict(causal=True)),
+]
+
+
+def _mutant(old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not unique/present: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new), "<oracle mutant>", "exec"), mod.__dict__)
+    return mod
+
+
+def _failures(mod, monkeypatch):
+    for name in ORACLE_NAMES:
+        monkeypatch.setattr(T, name, getattr(mod, name))
+    failed = []
+    for fn, kw in PINS:
+        try:
+            fn(**kw)
+        except Exception:  # noqa: BLE001 -- any failure means the pin caught it
+            failed.append(fn.__name__)
+    return failed
+
+
+def test_unmutated_copy_passes_every_pin(monkeypatch):
+    mod = _mutant("ROW_CHUNK = 2048", "ROW_CHUNK = 2048")
+    assert _failures(mod, monkeypatch) == []
+
+
+@pytest.mark.parametrize("label,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_planted_mistake(label, old, new, monkeypatch):
+    assert _failures(_mutant(old, new), monkeypatch), f"no pin caught: {label}"
