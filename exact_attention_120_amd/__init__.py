@@ -1,0 +1,118 @@
+"""MI355X (gfx950) IO-aware exact attention: Python binding of libfa.so.
+
+The functions named like the C ABI (``fa_fwd``, ``fa_bwd``,
+``fa_bwd_workspace_size``, ``fa_strerror``) only marshal arguments: they
+read shapes, dtype, device pointers and the current HIP stream from torch
+tensors and call the library, which does every step of the computation in
+its own kernels. ``forward``/``backward`` additionally allocate the outputs
+(and the backward workspace) with torch. There is no fallback: if libfa.so
+is missing, or a tensor is not on the GPU, these raise.
+"""
+
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+
+__all__ = ["FaError", "fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_strerror",
+           "forward", "backward", "DTYPES"]
+
+DTYPES = {torch.float32: _lib.FA_F32, torch.float16: _lib.FA_F16,
+          torch.bfloat16: _lib.FA_BF16}
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {fa_strerror(status)} (status {status})")
+
+
+def fa_strerror(status: int) -> str:
+    return _lib.load().fa_strerror(status).decode()
+
+
+def fa_bwd_workspace_size(B: int, H: int, N: int, d: int) -> int:
+    return int(_lib.load().fa_bwd_workspace_size(B, H, N, d))
+
+
+def _check(tensors: dict, shape, dtype) -> None:
+    for name, t in tensors.items():
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+            raise ValueError(f"{name}: expected contiguous {tuple(shape)} {dtype}, got "
+                             f"{tuple(t.shape)} {t.dtype} contiguous={t.is_contiguous()}")
+
+
+def _stream(t: torch.Tensor, stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream(t.device).cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _shape(q: torch.Tensor):
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    if q.dtype not in DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    return tuple(q.shape)
+
+
+def fa_fwd(q, k, v, o, lse, scale: float, causal: bool, stream=None) -> None:
+    """Enqueue the forward kernel: o, lse <- attention(q, k, v)."""
+    B, H, N, d = _shape(q)
+    _check({"q": q, "k": k, "v": v, "o": o}, (B, H, N, d), q.dtype)
+    _check({"lse": lse}, (B, H, N), torch.float32)
+    with torch.cuda.device(q.device):
+        st = _lib.load().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                lse.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
+                                DTYPES[q.dtype], _stream(q, stream))
+    if st != _lib.FA_OK:
+        raise FaError(st, "fa_fwd")
+
+
+def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool, workspace,
+           stream=None) -> None:
+    """Enqueue the backward kernels: dq, dk, dv <- gradients of sum(do * o)."""
+    B, H, N, d = _shape(q)
+    _check({"q": q, "k": k, "v": v, "o": o, "do": do, "dq": dq, "dk": dk, "dv": dv},
+           (B, H, N, d), q.dtype)
+    _check({"lse": lse}, (B, H, N), torch.float32)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    with torch.cuda.device(q.device):
+        st = _lib.load().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                dv.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
+                                DTYPES[q.dtype], workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), _stream(q, stream))
+    if st != _lib.FA_OK:
+        raise FaError(st, "fa_bwd")
+
+
+def _default_scale(d: int, scale):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def forward(q, k, v, causal: bool = False, scale: float | None = None, stream=None):
+    """Allocate O and LSE with torch and run fa_fwd; returns (o, lse)."""
+    B, H, N, d = _shape(q)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa_fwd(q, k, v, o, lse, _default_scale(d, scale), causal, stream)
+    return o, lse
+
+
+def backward(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None,
+             stream=None, workspace=None):
+    """Allocate dQ, dK, dV (and the workspace unless given) and run fa_bwd."""
+    B, H, N, d = _shape(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if workspace is None:
+        workspace = torch.empty(fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8,
+                                device=q.device)
+    fa_bwd(q, k, v, o, do, lse, dq, dk, dv, _default_scale(d, scale), causal, workspace, stream)
+    return dq, dk, dv

@@ -1,0 +1,121 @@
+// fa_api.cpp -- the exported C ABI (include/fa.h): argument validation,
+// workspace layout and dispatch to the kernel launchers. Every check runs on
+// the host before anything is enqueued, so a rejected call touches no device
+// state.
+#include "../../include/fa.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "fa_internal.hpp"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+size_t elem_size(int dtype) { return dtype == FA_F32 ? 4 : 2; }
+
+bool dtype_ok(int dtype) { return dtype == FA_F32 || dtype == FA_F16 || dtype == FA_BF16; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [p, p+n) and [q, q+m) intersect.
+bool overlap(const void* p, size_t n, const void* q, size_t m) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return a < b + m && b < a + n;
+}
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Shared shape checks. Returns FA_OK or the status to report.
+int check_shape(int B, int H, int N, int d, float scale, int causal, int dtype) {
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  const long long total = (long long)B * H * N * d;
+  if ((long long)N * d >= (1ll << 31) || total >= (1ll << 40)) return FA_ERR_UNSUPPORTED;
+  if (fa::fwd_grid_size(B, H, N) >= (1ll << 31)) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+           int N, int d, float scale, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  int st = check_shape(B, H, N, d, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  const size_t tb = (size_t)B * H * N * d * elem_size(dtype);
+  const size_t lb = (size_t)B * H * N * sizeof(float);
+  const void* ins[] = {q, k, v};
+  for (const void* in : ins)
+    if (overlap(o, tb, in, tb) || overlap(lse, lb, in, tb)) return FA_ERR_INVALID_ARG;
+  if (overlap(o, tb, lse, lb)) return FA_ERR_INVALID_ARG;
+
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, scale * kLog2e, causal, dtype};
+  return hip_status(fa::launch_fwd(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
+  const size_t rows = (size_t)B * H * N;
+  return round_up(rows * sizeof(float)) + round_up(rows * d * sizeof(float));
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+           const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+           float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
+           void* stream) {
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv || !workspace)
+    return FA_ERR_INVALID_ARG;
+  int st = check_shape(B, H, N, d, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  const void* ptrs[] = {q, k, v, o, dO, lse, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return FA_ERR_ALIGN;
+  const size_t need = fa_bwd_workspace_size(B, H, N, d);
+  if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+
+  const size_t tb = (size_t)B * H * N * d * elem_size(dtype);
+  const size_t lb = (size_t)B * H * N * sizeof(float);
+  struct Range { const void* p; size_t n; };
+  const Range ins[] = {{q, tb}, {k, tb}, {v, tb}, {o, tb}, {dO, tb}, {lse, lb}};
+  const Range outs[] = {{dq, tb}, {dk, tb}, {dv, tb}, {workspace, need}};
+  for (const Range& w : outs) {
+    for (const Range& r : ins)
+      if (overlap(w.p, w.n, r.p, r.n)) return FA_ERR_INVALID_ARG;
+    for (const Range& x : outs)
+      if (&x != &w && overlap(w.p, w.n, x.p, x.n)) return FA_ERR_INVALID_ARG;
+  }
+
+  char* ws = static_cast<char*>(workspace);
+  float* dsum = reinterpret_cast<float*>(ws);
+  float* dq_acc = reinterpret_cast<float*>(ws + round_up(lb));
+  fa::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, dsum, dq_acc,
+                B, H, N, d, scale, scale * kLog2e, causal, dtype};
+  return hip_status(fa::launch_bwd(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+const char* fa_strerror(int status) {
+  switch (status) {
+    case FA_OK: return "success";
+    case FA_ERR_INVALID_ARG: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported head dimension or size";
+    case FA_ERR_ALIGN: return "pointer not sufficiently aligned";
+    case FA_ERR_WORKSPACE: return "workspace too small";
+    case FA_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,128 @@
+// fa_device.hpp -- gfx950 (CDNA4) device helpers shared by the attention
+// kernels: vector types, matrix-core (MFMA) operand traits per element type,
+// packing of float32 probabilities into MFMA operands, the workgroup-to-XCD
+// remap, and raw LDS/global vector accesses.
+//
+// MFMA operand conventions used throughout (wave64, 32x32 output tiles):
+//   A (32 x K)  : lane l holds row (l & 31), K-elements [h*KH, h*KH + KH)
+//                 with h = l >> 5;
+//   B (K x 32)  : lane l holds column (l & 31), the same K-elements;
+//   C (32 x 32) : lane l, register r holds column (l & 31) and row
+//                 8*(r >> 2) + 4*h + (r & 3).
+// Only the pairing of A and B matters for the contraction, so any mapping of
+// the K index onto data is legal as long as both operands use it; the
+// kernels exploit that freedom to keep every operand a contiguous read.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Element traits. KH = operand elements one lane contributes to one MFMA
+// (half of the instruction's K depth); Raw = those elements as bits.
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<__bf16> {
+  static constexpr int KH = 8;
+  using Raw = u32x4;
+  __device__ static inline f32x16 mma(Raw a, Raw b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  // Round 8 floats to bf16 (nearest-even), pack them as one operand, and add
+  // the 8 *unrounded* values to acc: bf16's 2^-9 relative rounding would not
+  // average out in rows that see only a few keys, so the normalizer is kept
+  // in float32. Each pair is converted once (one v_cvt_pk_bf16_f32) and kept
+  // as its own 32-bit word: extracting pairs back out of a packed 8-element
+  // vector mis-compiles (every pair read as the first one).
+  __device__ static inline Raw pack_sum(const float* p, float& acc) {
+    Raw r;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const bf16x2 pr = {(__bf16)p[2 * w], (__bf16)p[2 * w + 1]};
+      acc += p[2 * w] + p[2 * w + 1];
+      r[w] = __builtin_bit_cast(uint32_t, pr);
+    }
+    return r;
+  }
+  __device__ static inline uint16_t bits(float x) {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+  }
+};
+
+template <>
+struct Elem<_Float16> {
+  static constexpr int KH = 8;
+  using Raw = u32x4;
+  __device__ static inline f32x16 mma(Raw a, Raw b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  // As for bf16, but the sum is taken over the rounded values with one
+  // dot product per pair: fp16 keeps 11 significant bits, so the rounded
+  // normalizer is accurate to 2^-12 relative, and it costs half the adds.
+  __device__ static inline Raw pack_sum(const float* p, float& acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    Raw r;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const f16x2 pr = {(_Float16)p[2 * w], (_Float16)p[2 * w + 1]};
+      acc = __builtin_amdgcn_fdot2(pr, one, acc, false);
+      r[w] = __builtin_bit_cast(uint32_t, pr);
+    }
+    return r;
+  }
+  __device__ static inline uint16_t bits(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+  }
+};
+
+template <>
+struct Elem<float> {
+  static constexpr int KH = 1;
+  using Raw = uint32_t;
+  __device__ static inline f32x16 mma(Raw a, Raw b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a),
+                                               __builtin_bit_cast(float, b), c, 0, 0, 0);
+  }
+  __device__ static inline Raw pack_sum(const float* p, float& acc) {
+    acc += p[0];
+    return __builtin_bit_cast(Raw, p[0]);
+  }
+};
+
+// Raw loads/stores of KH elements (16 bytes for 16-bit types, 4 for f32).
+template <typename Raw>
+__device__ inline Raw ld(const void* p) {
+  return *reinterpret_cast<const Raw*>(p);
+}
+template <typename Raw>
+__device__ inline void st(void* p, Raw x) {
+  *reinterpret_cast<Raw*>(p) = x;
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (bid % 8). Remap so
+// that consecutive logical tiles (the query tiles of one head, which read the
+// same K/V) land on the same XCD and share its L2. A bijection on [0, total).
+__device__ inline int xcd_remap(int bid, int total) {
+  constexpr int X = 8;
+  const int per = total / X, rem = total % X;
+  const int x = bid % X, idx = bid / X;
+  return x * per + (x < rem ? x : rem) + idx;
+}
+
+}  // namespace fa

@@ -1,0 +1,51 @@
+// fa_internal.hpp -- argument blocks and launchers shared between the C-ABI
+// layer (fa_api.cpp) and the kernel translation units. Host-visible only
+// through this header; nothing here is exported from libfa.so.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+
+namespace fa {
+
+// Forward: contiguous [B,H,N,d] tensors, [B,H,N] float32 LSE.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, N, d;
+  float scale;       // softmax scale (>= 0)
+  float scale_log2;  // scale * log2(e)
+  int causal;
+  int dtype;         // fa_dtype
+};
+
+// Backward: forward tensors plus dO and the gradient outputs. `dsum` is the
+// float32 [B,H,N] row term D, `dq_acc` the float32 [B,H,N,d] dQ accumulator.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dsum;
+  float* dq_acc;
+  int B, H, N, d;
+  float scale;
+  float scale_log2;
+  int causal;
+  int dtype;
+};
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+
+long long fwd_grid_size(int B, int H, int N);
+
+}  // namespace fa

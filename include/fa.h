@@ -1,0 +1,134 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) IO-aware exact attention library
+ * (libfa.so).
+ *
+ * The operation is exact scaled-dot-product attention,
+ *     O = softmax(scale * Q K^T [+ causal mask]) V,
+ * computed the IO-aware way: the N x N score and probability matrices live
+ * only on chip, tile by tile, with an online softmax, and only O plus one
+ * log-sum-exp per query row are written back. The backward pass recomputes
+ * the probabilities on chip from that log-sum-exp.
+ *
+ * Sources:
+ *   "FlashAttention原理：从原始Attention到FlashAttention"
+ *     (blog.csdn.net/qq_43527718/article/details/142302113):
+ *     section 二.2 -- the standard (unfused) pipeline whose result must be
+ *     reproduced exactly; section 二.5/二.6 -- tiling and blockwise softmax;
+ *     section 二.7 -- query blocks in the outer loop, key/value blocks in the
+ *     inner loop, fully masked blocks skipped; section 一.2 -- the softmax
+ *     normalizer is stored so the backward pass can recompute attention on
+ *     chip instead of reading it from HBM.
+ *   "FlashAttention：优化大模型训练的内存与计算效率" (cnnetsun.cn/a/3461300):
+ *     section 3.1 -- tensors shaped (batch, heads, seq_len, dim) and the
+ *     is_causal switch; section 4.1 -- softmax kept in float32 under
+ *     mixed precision.
+ *
+ * Conventions shared by every entry point:
+ *   - Layout: Q, K, V, O, dO, dQ, dK, dV are contiguous row-major
+ *     [B, H, N, d] device arrays of one element type (``dtype``); LSE is a
+ *     contiguous [B, H, N] float32 device array. Self-attention: queries and
+ *     keys share the length N.
+ *   - Causal: when ``causal`` is 1, key j is hidden from query i if j > i.
+ *   - LSE_i = ln(sum_j exp(scale * q_i . k_j)) over the visible keys
+ *     (natural log of the scaled scores' exponential sum).
+ *   - Ownership: the caller allocates and owns every buffer (device memory).
+ *     The library allocates no device memory, frees nothing and keeps no
+ *     pointer after returning. Inputs are read-only; outputs must not overlap
+ *     any input or each other.
+ *   - Streams: ``stream`` is a hipStream_t (NULL = the null stream). Every
+ *     call only enqueues work on it and returns; the results are ready when
+ *     the stream is synchronized. The returned status covers argument
+ *     validation and the kernel launches; a fault inside a kernel surfaces at
+ *     the caller's next synchronization.
+ *   - Supported: d in {64, 128}; dtype FA_F32, FA_F16, FA_BF16; any N >= 1;
+ *     B*H*N*d < 2^40 elements and N*d < 2^31. Arithmetic: products of
+ *     16-bit inputs on bf16/fp16 matrix cores (fp32 matrix cores for FA_F32)
+ *     with float32 accumulation; softmax statistics in float32; outputs
+ *     rounded to nearest-even into ``dtype``.
+ *   - Thread safety: no global mutable state; concurrent calls on different
+ *     streams are independent.
+ *   - Validation (in order; the first failure is returned and nothing is
+ *     enqueued): null pointers, B/H/N < 1 or dtype unknown or causal not 0/1
+ *     or scale negative/non-finite -> FA_ERR_INVALID_ARG; d not supported or
+ *     sizes too large -> FA_ERR_UNSUPPORTED; a pointer not 16-byte aligned
+ *     -> FA_ERR_ALIGN; overlapping output/input ranges -> FA_ERR_INVALID_ARG;
+ *     workspace too small -> FA_ERR_WORKSPACE.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of Q, K, V, O, dO, dQ, dK, dV. */
+typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
+
+/* Status codes. */
+enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1,
+  FA_ERR_UNSUPPORTED = -2,
+  FA_ERR_ALIGN = -3,
+  FA_ERR_WORKSPACE = -4,
+  FA_ERR_HIP = -5
+};
+
+/*
+ * fa_fwd -- forward attention.
+ *   q, k, v : [B,H,N,d] ``dtype`` inputs (device, read-only).
+ *   o       : [B,H,N,d] ``dtype`` output (device).
+ *   lse     : [B,H,N] float32 output (device): the per-row log-sum-exp the
+ *             backward pass needs (the stored softmax normalizer of the
+ *             pages' section 一.2).
+ *   scale   : multiplier of Q K^T; finite and >= 0 (1/sqrt(d) usually).
+ *   causal  : 0 or 1.
+ *   dtype   : an fa_dtype value.
+ *   stream  : hipStream_t to enqueue on.
+ * One kernel: query tiles in the outer (grid) dimension, key/value tiles in
+ * the inner loop, online softmax in registers; tiles above the causal
+ * diagonal are never visited.
+ * Returns FA_OK or a negative status (see the conventions above).
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal, int dtype,
+           void* stream);
+
+/*
+ * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs:
+ * a float32 [B,H,N] row term D_i = sum_k dO_ik O_ik and a float32
+ * [B,H,N,d] dQ accumulator, each 256-byte aligned. Returns 0 for invalid
+ * sizes.
+ */
+size_t fa_bwd_workspace_size(int B, int H, int N, int d);
+
+/*
+ * fa_bwd -- backward attention for the loss sum(dO * O).
+ *   q, k, v, o, dO : [B,H,N,d] ``dtype`` (device, read-only); o is the
+ *                    forward output.
+ *   lse            : [B,H,N] float32 from fa_fwd (device, read-only).
+ *   dq, dk, dv     : [B,H,N,d] ``dtype`` outputs (device).
+ *   workspace      : device scratch of at least fa_bwd_workspace_size()
+ *                    bytes, 256-byte aligned, owned by the caller; its
+ *                    contents on entry are ignored (the library clears what
+ *                    it needs on ``stream``) and undefined on exit.
+ *   other arguments as for fa_fwd (scale and causal must match the forward).
+ * The probabilities are recomputed on chip from Q, K and LSE (never read
+ * from memory); key/value tiles are the outer (grid) dimension, query tiles
+ * the inner loop, and dQ is accumulated in float32 in the workspace.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const void* dO, const float* lse, void* dq, void* dk, void* dv,
+           int B, int H, int N, int d, float scale, int causal, int dtype,
+           void* workspace, size_t workspace_bytes, void* stream);
+
+/* fa_strerror -- static, NUL-terminated description of a status code. */
+const char* fa_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

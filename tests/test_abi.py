@@ -1,0 +1,128 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/fa.h declares, and rejects bad arguments before touching the device.
+
+Every call below carries exactly one defect, so validation returns before any
+HIP call; the fake addresses are never dereferenced. No call here has valid
+arguments (that would launch a kernel).
+"""
+
+import ctypes
+
+import pytest
+
+from exact_attention_120_amd import _lib
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_WORKSPACE, FA_ERR_HIP = (
+    0, -1, -2, -3, -4, -5)
+
+# Distinct, 256-byte aligned fake addresses far apart (never dereferenced).
+Q, K, V, O, LSE, DO, DQ, DK, DV, WS = (0x10_0000_0000 + i * 0x1_0000_0000 for i in range(10))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_functions_are_exported(lib):
+    names = _lib.header_functions()
+    assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_strerror"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_strerror(lib):
+    for st in (FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_WORKSPACE,
+               FA_ERR_HIP):
+        assert lib.fa_strerror(st) and lib.fa_strerror(st) != b"unknown status"
+    assert lib.fa_strerror(12345) == b"unknown status"
+
+
+def fwd(lib, q=Q, k=K, v=V, o=O, lse=LSE, B=1, H=2, N=16, d=64, scale=0.125, causal=0,
+        dtype=2):
+    return lib.fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, None)
+
+
+FWD_CASES = [
+    (dict(q=None), FA_ERR_INVALID_ARG),
+    (dict(lse=None), FA_ERR_INVALID_ARG),
+    (dict(B=0), FA_ERR_INVALID_ARG),
+    (dict(H=-1), FA_ERR_INVALID_ARG),
+    (dict(N=0), FA_ERR_INVALID_ARG),
+    (dict(dtype=7), FA_ERR_INVALID_ARG),
+    (dict(causal=2), FA_ERR_INVALID_ARG),
+    (dict(scale=-0.5), FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), FA_ERR_INVALID_ARG),
+    (dict(d=32), FA_ERR_UNSUPPORTED),
+    (dict(d=96), FA_ERR_UNSUPPORTED),
+    (dict(N=1 << 24, d=128), FA_ERR_UNSUPPORTED),          # N*d >= 2^31
+    (dict(B=1 << 12, H=1 << 12, N=1 << 16), FA_ERR_UNSUPPORTED),  # total >= 2^40
+    (dict(q=Q + 8), FA_ERR_ALIGN),
+    (dict(o=O + 2), FA_ERR_ALIGN),
+    (dict(lse=LSE + 4), FA_ERR_ALIGN),
+    (dict(o=Q), FA_ERR_INVALID_ARG),                        # output aliases input
+    (dict(o=K + 1024), FA_ERR_INVALID_ARG),                 # output overlaps input
+    (dict(lse=V + 16), FA_ERR_INVALID_ARG),
+    (dict(lse=O + 256), FA_ERR_INVALID_ARG),                # lse overlaps o
+]
+
+
+@pytest.mark.parametrize("kw,status", FWD_CASES)
+def test_fwd_rejects(lib, kw, status):
+    assert fwd(lib, **kw) == status
+
+
+def test_workspace_size(lib):
+    B, H, N, d = 2, 3, 100, 64
+    rows = B * H * N
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert lib.fa_bwd_workspace_size(B, H, N, d) == up(rows * 4) + up(rows * d * 4)
+    assert lib.fa_bwd_workspace_size(0, H, N, d) == 0
+    assert lib.fa_bwd_workspace_size(B, H, N, 80) == 0
+
+
+def bwd(lib, q=Q, k=K, v=V, o=O, do=DO, lse=LSE, dq=DQ, dk=DK, dv=DV, B=1, H=2, N=16, d=64,
+        scale=0.125, causal=1, dtype=1, ws=WS, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_bwd_workspace_size(B, H, N, d) if d in (64, 128) else 1 << 20
+    return lib.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, ws,
+                      ws_bytes, None)
+
+
+BWD_CASES = [
+    (dict(do=None), FA_ERR_INVALID_ARG),
+    (dict(ws=None), FA_ERR_INVALID_ARG),
+    (dict(N=0), FA_ERR_INVALID_ARG),
+    (dict(scale=-1.0), FA_ERR_INVALID_ARG),
+    (dict(d=256), FA_ERR_UNSUPPORTED),
+    (dict(dk=DK + 4), FA_ERR_ALIGN),
+    (dict(ws=WS + 16), FA_ERR_ALIGN),                       # workspace needs 256 B
+    (dict(ws_bytes=1024), FA_ERR_WORKSPACE),
+    (dict(dq=Q), FA_ERR_INVALID_ARG),
+    (dict(dv=DK), FA_ERR_INVALID_ARG),                      # two outputs alias
+    (dict(ws=DO), FA_ERR_INVALID_ARG),                      # workspace overlaps an input
+]
+
+
+@pytest.mark.parametrize("kw,status", BWD_CASES)
+def test_bwd_rejects(lib, kw, status):
+    assert bwd(lib, **kw) == status
+
+
+def test_signatures_match_header_argument_counts():
+    import re
+    text = open(_lib.HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    for name, (_, args) in _lib.SIGNATURES.items():
+        m = re.search(name + r"\s*\(([^)]*)\)", text)
+        assert m, name
+        n_params = len([p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"])
+        assert n_params == len(args), name
+
+
+def test_library_is_native_shared_object():
+    with open(_lib.LIB_PATH, "rb") as f:
+        assert f.read(4) == b"\x7fELF"
+    assert isinstance(_lib.load(), ctypes.CDLL)
