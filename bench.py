@@ -1,0 +1,267 @@
+"""Benchmark of the IO-aware exact attention hot path on one MI355X.
+
+Default run (no flags): N=1 GPU, the long-sequence bf16 workload
+B=1 H=16 N=16384 d=128 (non-causal), Q/K/V ~ N(0,1) from seed 0. One step =
+one forward pass (fa_fwd) plus one backward pass (fa_bwd) over that batch,
+inputs already resident in HBM. Prints ONE JSON line.
+
+FLOP convention: forward 4*B*H*N^2*d (halved when causal); backward 2.5x
+the forward. value = (fwd + bwd FLOP) / step time, in TFLOP/s.
+
+Roofline: the forward kernel (one launch per fa_fwd call) is timed with HIP
+events around every launch in the timed region, on the stream it runs on;
+achieved = its algorithmic FLOP per launch / its mean duration, against the
+MI355X dense bf16/fp16 MFMA peak (2.5 PFLOP/s; fp32 MFMA: 157.3 TFLOP/s).
+`traffic` (measured HBM bytes per launch) is read from the committed
+rocprofv3 counter summary only when that summary was taken from the current
+kernel sources (their hash is recorded in it), else null.
+
+cpu_baseline: the CPU oracle (float64 numpy) on a bounded sample of the same
+workload -- whole heads, forward and backward, until ~10 s have elapsed --
+reported in the same unit.
+
+Other modes (used to collect the rocprofv3 summaries under profiles/):
+  --only fwd|bwd        time only that direction (no CPU baseline)
+  --sweep               forward over N in {1k,2k,4k,8k,16k}, B=1 H=16 d=128
+  --copy-bytes BYTES    a plain device copy of BYTES bytes (counter scaling)
+  --summarize DIR       turn rocprofv3 output under DIR into a text table
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd/bwd TFLOP/s (bf16, N=4k-16k, d=128) and % of MFMA peak"
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}  # MI355X dense MFMA
+KERNEL_SOURCES = ["exact_attention_120_amd/csrc/fa_fwd.hip",
+                  "exact_attention_120_amd/csrc/fa_device.hpp"]
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fa_fwd_bf16_n16k_d128_hbm_traffic.md")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """Per-launch HBM bytes from the committed counter summary, if current."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    text = open(TRAFFIC_SUMMARY).read()
+    m_hash = re.search(r"kernel-source-hash:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm-bytes-per-launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(w, inputs, budget_s=10.0, max_s=30.0):
+    """Time the float64 oracle (fwd + bwd) over whole heads of the workload."""
+    import numpy as np
+    import threadpoolctl
+
+    from fa_inputs import to_f64
+    from oracle import attention_backward, attention_forward
+
+    q, k, v, do = (to_f64(inputs[n]) for n in ("q", "k", "v", "do"))
+    q, k, v, do = (x.reshape(-1, w.N, w.d) for x in (q, k, v, do))
+    heads, flop, t0 = 0, 0.0, time.perf_counter()
+    per_head = (w.fwd_flops() + w.bwd_flops()) / (w.B * w.H)
+    while heads < q.shape[0]:
+        o, _ = attention_forward(q[heads], k[heads], v[heads], w.scale, w.causal)
+        attention_backward(q[heads], k[heads], v[heads], do[heads], w.scale, w.causal)
+        np.asarray(o)
+        heads += 1
+        flop += per_head
+        el = time.perf_counter() - t0
+        if el >= budget_s or el + el / heads > max_s:
+            break
+    el = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
+    return {"value": flop / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"float64 numpy oracle, forward + backward of {heads} of {w.B * w.H} "
+                      f"heads (all {w.N} rows each) of this workload, {el:.1f} s; host has "
+                      f"{len(os.sched_getaffinity(0))} cores, BLAS threads {threads}"}
+
+
+def time_calls(fn, steps, warmup, events_per_call):
+    """Run fn() warmup+steps times; returns (total_ms, [per-call event ms lists])."""
+    import torch
+
+    for _ in range(warmup):
+        fn(None)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(events_per_call + 1)]
+          for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        fn(ev[i])
+    end.record()
+    torch.cuda.synchronize()
+    total = start.elapsed_time(end)
+    per = [[e[j].elapsed_time(e[j + 1]) for e in ev] for j in range(events_per_call)]
+    return total, per
+
+
+def run_main(args):
+    import torch
+
+    import exact_attention_120_amd as fa
+    from fa_inputs import WORKLOADS, workload_inputs
+
+    w = WORKLOADS[args.workload]
+    if w.dtype != "bf16" and args.workload == "bf16_n16k_d128":
+        raise SystemExit("unexpected workload table")
+    inp = workload_inputs(type(w)(**{**w.__dict__, "backward": True}))
+    dev = torch.device("cuda:0")
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    B, H, N, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device=dev)
+    do_fwd, do_bwd = args.only in (None, "fwd"), args.only in (None, "bwd")
+    if do_bwd:  # the backward needs a forward output
+        fa.fa_fwd(q, k, v, o, lse, w.scale, w.causal)
+        torch.cuda.synchronize()
+
+    def step(ev):
+        j = 0
+        if ev is not None:
+            ev[j].record()
+        if do_fwd:
+            fa.fa_fwd(q, k, v, o, lse, w.scale, w.causal)
+            if ev is not None:
+                j += 1
+                ev[j].record()
+        if do_bwd:
+            fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, w.scale, w.causal, ws)
+            if ev is not None:
+                j += 1
+                ev[j].record()
+
+    n_ev = int(do_fwd) + int(do_bwd)
+    total_ms, per = time_calls(step, args.steps, args.warmup, n_ev)
+    ms_step = total_ms / args.steps
+    fwd_flop, bwd_flop = w.fwd_flops(), w.bwd_flops()
+    flop = fwd_flop * do_fwd + bwd_flop * do_bwd
+    peak = PEAK_TFLOPS[w.dtype]
+    out = {
+        "metric": METRIC, "value": flop / (ms_step * 1e-3) / 1e12, "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
+                   "step": "+".join(x for x, on in (("fwd", do_fwd), ("bwd", do_bwd)) if on),
+                   "inputs": "Q,K,V,dO ~ N(0,1) float32 from seed 0, rounded to bf16"},
+        "frac_of_peak": flop / (ms_step * 1e-3) / 1e12 / peak,
+    }
+    j = 0
+    if do_fwd:
+        f_ms = sum(per[j]) / len(per[j])
+        f_tf = fwd_flop / (f_ms * 1e-3) / 1e12
+        out["fwd"] = {"ms": f_ms, "tflops": f_tf, "frac_of_peak": f_tf / peak}
+        out["roofline"] = {"bound": "mfma", "achieved": f_tf, "peak": peak, "unit": "TFLOP/s",
+                           "frac": f_tf / peak, "traffic": read_traffic(),
+                           "kernel": "fwd_kernel (one launch per fa_fwd)",
+                           "flop_per_launch": fwd_flop}
+        j += 1
+    if do_bwd:
+        b_ms = sum(per[j]) / len(per[j])
+        b_tf = bwd_flop / (b_ms * 1e-3) / 1e12
+        out["bwd"] = {"ms": b_ms, "tflops": b_tf, "frac_of_peak": b_tf / peak,
+                      "note": "all backward kernels of one fa_bwd call"}
+    if args.only is None and not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(out), flush=True)
+
+
+def run_sweep(args):
+    import torch
+
+    import exact_attention_120_amd as fa
+    from fa_inputs import make_inputs
+
+    for n in (1024, 2048, 4096, 8192, 16384):
+        for causal in (False, True):
+            inp = make_inputs(1, 16, n, 128, "bf16", seed=0)
+            q, k, v = (inp[x].to("cuda:0") for x in ("q", "k", "v"))
+            o, lse = torch.empty_like(q), torch.empty((1, 16, n), device="cuda:0")
+            for _ in range(3):
+                fa.fa_fwd(q, k, v, o, lse, 128 ** -0.5, causal)
+            torch.cuda.synchronize()
+            print(json.dumps({"sweep_N": n, "causal": causal}), flush=True)
+
+
+def run_copy(args):
+    import torch
+
+    n = args.copy_bytes // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n * 4}), flush=True)
+
+
+def summarize(path):
+    """Print per-kernel averages from rocprofv3 CSV output found under path."""
+    rows = []
+    for f in glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    agg = {}
+    for r in rows:
+        key = (r.get("Kernel_Name", "?")[:90], r.get("Grid_Size", ""), r.get("Counter_Name", ""))
+        agg.setdefault(key, []).append(float(r.get("Counter_Value", 0)))
+    print("| kernel | grid | counter | dispatches | mean value |")
+    print("|---|---|---|---|---|")
+    for (kname, grid, cname), vals in sorted(agg.items()):
+        print(f"| {kname} | {grid} | {cname} | {len(vals)} | {sum(vals) / len(vals):.6g} |")
+
+
+def main():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="bf16_n16k_d128")
+    p.add_argument("--only", choices=["fwd", "bwd"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--sweep", action="store_true")
+    p.add_argument("--copy-bytes", type=int)
+    p.add_argument("--summarize")
+    args = p.parse_args()
+    if args.summarize:
+        return summarize(args.summarize)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(heads shard across GPUs with no communication; see the design notes)",
+              file=sys.stderr)
+        raise SystemExit(2)
+    if args.copy_bytes:
+        return run_copy(args)
+    if args.sweep:
+        return run_sweep(args)
+    return run_main(args)
+
+
+if __name__ == "__main__":
+    main()

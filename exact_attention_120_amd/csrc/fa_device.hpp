@@ -115,6 +115,20 @@ __device__ inline void st(void* p, Raw x) {
   *reinterpret_cast<Raw*>(p) = x;
 }
 
+// When a 32x32 C tile (scores, or score gradients) becomes the B operand of
+// the next product, register r of lane half h holds row 8*(r>>2) + 4*h + (r&3)
+// of each 32-row block, and MFMA number u takes registers [u*KH, u*KH+KH).
+// vt_pos gives, for row `idx` of a tile, the position at which the matching
+// A operand must store it (in a transposed LDS copy) so that both operands
+// walk the contraction in the same order and every A read is contiguous.
+template <int KH>
+__device__ constexpr int vt_pos(int idx) {
+  const int blk = idx >> 5, kb = idx & 31;
+  const int h = (kb >> 2) & 1;
+  const int r = 4 * (kb >> 3) + (kb & 3);
+  return blk * 32 + (r / KH) * (2 * KH) + h * KH + (r % KH);
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs (bid % 8). Remap so
 // that consecutive logical tiles (the query tiles of one head, which read the
 // same K/V) land on the same XCD and share its L2. A bijection on [0, total).

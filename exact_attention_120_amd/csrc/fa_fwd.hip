@@ -62,17 +62,6 @@ struct FwdShape {
   static_assert(kBN * D / EPV % kThreads == 0, "K tile must split evenly");
 };
 
-// Position of key `key` (0..kBN-1) in a V^T row: the order in which the
-// score registers are handed to the PV MFMA as its B operand (register r of
-// a 32-key block holds key 8*(r>>2) + 4*h + (r&3) in lane half h).
-template <int KH>
-__device__ constexpr int vt_pos(int key) {
-  const int mt = key >> 5, kb = key & 31;
-  const int h = (kb >> 2) & 1;
-  const int r = 4 * (kb >> 3) + (kb & 3);
-  return mt * 32 + (r / KH) * (2 * KH) + h * KH + (r % KH);
-}
-
 template <typename T, int D>
 struct TileLoader {
   using S = FwdShape<T, D>;
