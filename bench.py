@@ -8,13 +8,18 @@ inputs already resident in HBM. Prints ONE JSON line.
 FLOP convention: forward 4*B*H*N^2*d (halved when causal); backward 2.5x
 the forward. value = (fwd + bwd FLOP) / step time, in TFLOP/s.
 
-Roofline: the forward kernel (one launch per fa_fwd call) is timed with HIP
-events around every launch in the timed region, on the stream it runs on;
-achieved = its algorithmic FLOP per launch / its mean duration, against the
+Roofline: every fa_fwd and fa_bwd call in the timed region is bracketed by
+HIP events on the stream it runs on. fa_fwd is one kernel; fa_bwd is three,
+of which the main kernel holds all the matrix work (the row-term and dQ
+conversion kernels are memory-bound and take well under 1% of the call, per
+the committed rocprofv3 trace). `roofline` describes the direction that
+takes longer (the dominant kernel); `roofline_fwd` / `roofline_bwd` give
+both. achieved = algorithmic FLOP per call / mean call duration, against the
 MI355X dense bf16/fp16 MFMA peak (2.5 PFLOP/s; fp32 MFMA: 157.3 TFLOP/s).
-`traffic` (measured HBM bytes per launch) is read from the committed
-rocprofv3 counter summary only when that summary was taken from the current
-kernel sources (their hash is recorded in it), else null.
+`traffic` (measured HBM bytes per call: FETCH_SIZE and WRITE_SIZE scaled by
+what the same counters read for a plain copy of known size) is read from the
+committed rocprofv3 counter summary only when that summary was taken from
+the current kernel sources (their hash is recorded in it), else null.
 
 cpu_baseline: the CPU oracle (float64 numpy) on a bounded sample of the same
 workload -- whole heads, forward and backward, until ~10 s have elapsed --
@@ -44,27 +49,29 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd/bwd TFLOP/s (bf16, N=4k-16k, d=128) and % of MFMA peak"
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}  # MI355X dense MFMA
-KERNEL_SOURCES = ["exact_attention_120_amd/csrc/fa_fwd.hip",
-                  "exact_attention_120_amd/csrc/fa_device.hpp"]
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fa_fwd_bf16_n16k_d128_hbm_traffic.md")
+KERNEL_SOURCES = {
+    "fwd": ["exact_attention_120_amd/csrc/fa_fwd.hip", "exact_attention_120_amd/csrc/fa_device.hpp"],
+    "bwd": ["exact_attention_120_amd/csrc/fa_bwd.hip", "exact_attention_120_amd/csrc/fa_device.hpp"],
+}
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fa_bf16_n16k_d128_hbm_traffic.md")
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(direction: str) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[direction]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic():
-    """Per-launch HBM bytes from the committed counter summary, if current."""
-    if not os.path.exists(TRAFFIC_SUMMARY):
+def read_traffic(direction: str, workload: str):
+    """Per-call HBM bytes from the committed counter summary, if current."""
+    if workload != "bf16_n16k_d128" or not os.path.exists(TRAFFIC_SUMMARY):
         return None
     text = open(TRAFFIC_SUMMARY).read()
-    m_hash = re.search(r"kernel-source-hash:\s*([0-9a-f]+)", text)
-    m_bytes = re.search(r"hbm-bytes-per-launch:\s*([0-9.eE+]+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+    m_hash = re.search(direction + r"-kernel-source-hash:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(direction + r"-hbm-bytes-per-call:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash(direction):
         return None
     return float(m_bytes.group(1))
 
@@ -172,21 +179,24 @@ def run_main(args):
                    "inputs": "Q,K,V,dO ~ N(0,1) float32 from seed 0, rounded to bf16"},
         "frac_of_peak": flop / (ms_step * 1e-3) / 1e12 / peak,
     }
-    j = 0
-    if do_fwd:
-        f_ms = sum(per[j]) / len(per[j])
-        f_tf = fwd_flop / (f_ms * 1e-3) / 1e12
-        out["fwd"] = {"ms": f_ms, "tflops": f_tf, "frac_of_peak": f_tf / peak}
-        out["roofline"] = {"bound": "mfma", "achieved": f_tf, "peak": peak, "unit": "TFLOP/s",
-                           "frac": f_tf / peak, "traffic": read_traffic(),
-                           "kernel": "fwd_kernel (one launch per fa_fwd)",
-                           "flop_per_launch": fwd_flop}
+    j, roofs = 0, {}
+    for name, on, fl, kern in (
+            ("fwd", do_fwd, fwd_flop, "fwd_kernel (the one kernel of fa_fwd)"),
+            ("bwd", do_bwd, bwd_flop, "fa_bwd: bwd_main_kernel (all MFMA work) + bwd_pre_kernel"
+                                      " + bwd_dq_kernel (memory-bound, <1% of the call)")):
+        if not on:
+            continue
+        ms = sum(per[j]) / len(per[j])
+        tf = fl / (ms * 1e-3) / 1e12
+        out[name] = {"ms": ms, "tflops": tf, "frac_of_peak": tf / peak}
+        roofs[name] = {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s",
+                       "frac": tf / peak, "traffic": read_traffic(name, w.name),
+                       "kernel": kern, "flop_per_call": fl, "ms_per_call": ms}
         j += 1
-    if do_bwd:
-        b_ms = sum(per[j]) / len(per[j])
-        b_tf = bwd_flop / (b_ms * 1e-3) / 1e12
-        out["bwd"] = {"ms": b_ms, "tflops": b_tf, "frac_of_peak": b_tf / peak,
-                      "note": "all backward kernels of one fa_bwd call"}
+    dominant = max(roofs, key=lambda n: roofs[n]["ms_per_call"])
+    out["roofline"] = dict(roofs[dominant], direction=dominant)
+    for name, r in roofs.items():
+        out["roofline_" + name] = r
     if args.only is None and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(out), flush=True)
@@ -221,20 +231,39 @@ def run_copy(args):
     print(json.dumps({"copy_bytes": n * 4}), flush=True)
 
 
+def _short(name: str) -> str:
+    """Readable kernel name from a (possibly mangled) symbol."""
+    m = re.search(r"(fwd_kernel|bwd_main_kernel|bwd_pre_kernel|bwd_dq_kernel)I([^E]*)", name)
+    if m:
+        return m.group(1) + "<" + m.group(2).replace("DF16b", "bf16,").replace("DF16_", "f16,")\
+            .replace("Li", "d=").replace("Lb0", ",noncausal").replace("Lb1", ",causal") + ">"
+    return name[:70]
+
+
 def summarize(path):
-    """Print per-kernel averages from rocprofv3 CSV output found under path."""
+    """Print per-kernel tables from rocprofv3 CSV output found under path."""
+    for f in sorted(glob.glob(os.path.join(path, "**", "*kernel_stats.csv"), recursive=True)):
+        print("| kernel | calls | average ns | min ns | max ns | % time |")
+        print("|---|---|---|---|---|---|")
+        for r in csv.DictReader(open(f)):
+            print(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                  f"{r['MinNs']} | {r['MaxNs']} | {float(r['Percentage']):.2f} |")
     rows = []
     for f in glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True):
         with open(f) as fh:
             rows += list(csv.DictReader(fh))
-    agg = {}
-    for r in rows:
-        key = (r.get("Kernel_Name", "?")[:90], r.get("Grid_Size", ""), r.get("Counter_Name", ""))
-        agg.setdefault(key, []).append(float(r.get("Counter_Value", 0)))
-    print("| kernel | grid | counter | dispatches | mean value |")
-    print("|---|---|---|---|---|")
-    for (kname, grid, cname), vals in sorted(agg.items()):
-        print(f"| {kname} | {grid} | {cname} | {len(vals)} | {sum(vals) / len(vals):.6g} |")
+    if rows:
+        agg = {}
+        for r in rows:
+            key = (_short(r.get("Kernel_Name", "?")), r.get("Grid_Size", ""),
+                   r.get("Counter_Name", ""))
+            agg.setdefault(key, []).append(float(r.get("Counter_Value", 0)))
+        print("| kernel | grid | counter | dispatches | mean value per dispatch |")
+        print("|---|---|---|---|---|")
+        for (kname, grid, cname), vals in sorted(agg.items()):
+            print(f"| {kname} | {grid} | {cname} | {len(vals)} | {sum(vals) / len(vals):.6g} |")
+    for d in ("fwd", "bwd"):
+        print(f"{d}-kernel-source-hash (current tree): {kernel_source_hash(d)}")
 
 
 def main():
