@@ -4,6 +4,7 @@
 // state.
 #include "../../include/fa.h"
 
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -12,6 +13,11 @@
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// The kernels' exponent multiplier scale*log2(e). It is kept >= FLT_MIN so
+// that a hidden score (-inf) always maps to exp2(-inf) = 0; for scale = 0 the
+// finite scores then give exp2(~1e-35) = 1 exactly, as they should.
+float exp2_scale(float scale) { return fmaxf(scale * kLog2e, FLT_MIN); }
 
 size_t elem_size(int dtype) { return dtype == FA_F32 ? 4 : 2; }
 
@@ -35,8 +41,11 @@ int check_shape(int B, int H, int N, int d, float scale, int causal, int dtype) 
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  // One head's slab is addressed with 32-bit byte offsets (plus one tile of
+  // overrun past N); the whole problem with 64-bit ones.
   const long long total = (long long)B * H * N * d;
-  if ((long long)N * d >= (1ll << 31) || total >= (1ll << 40)) return FA_ERR_UNSUPPORTED;
+  if ((long long)N * d * elem_size(dtype) > (1ll << 31) - (1ll << 20) || total >= (1ll << 40))
+    return FA_ERR_UNSUPPORTED;
   if (fa::fwd_grid_size(B, H, N) >= (1ll << 31)) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
@@ -61,7 +70,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     if (overlap(o, tb, in, tb) || overlap(lse, lb, in, tb)) return FA_ERR_INVALID_ARG;
   if (overlap(o, tb, lse, lb)) return FA_ERR_INVALID_ARG;
 
-  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, scale * kLog2e, causal, dtype};
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, exp2_scale(scale), causal, dtype};
   return hip_status(fa::launch_fwd(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -102,7 +111,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   float* dsum = reinterpret_cast<float*>(ws);
   float* dq_acc = reinterpret_cast<float*>(ws + round_up(lb));
   fa::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, dsum, dq_acc,
-                B, H, N, d, scale, scale * kLog2e, causal, dtype};
+                B, H, N, d, scale, exp2_scale(scale), causal, dtype};
   return hip_status(fa::launch_bwd(a, reinterpret_cast<hipStream_t>(stream)));
 }
 

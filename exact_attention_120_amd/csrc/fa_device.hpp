@@ -129,6 +129,50 @@ __device__ constexpr int vt_pos(int idx) {
   return blk * 32 + (r / KH) * (2 * KH) + h * KH + (r % KH);
 }
 
+// Raw buffer access to one head's [N, D] slab: loads at byte offsets at or
+// past `bytes` return zeros (the hardware range check), so tail rows need
+// no branches. The descriptor lives in scalar registers (uniform base).
+struct HeadBuf {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ HeadBuf(const void* base, uint32_t bytes)
+      : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000)) {}
+  __device__ inline u32x4 ld16(int byte_off) const {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+  }
+  __device__ inline uint32_t ld4(int byte_off) const {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0);
+  }
+};
+
+// Transposing LDS read (ds_read_b64_tr_b16, gfx950). Within each group of 16
+// lanes, output lane i receives, as its element r (r = 0..3), element (i % 4)
+// of the 8-byte chunk addressed by lane 4*r + i/4 of the group. So when lane
+// 4*r + q addresses row R_r, columns [c + 4q, c + 4q + 4) of a row-major
+// 16-bit tile, lane i ends up holding column c + i of rows R_0..R_3: a
+// column-major (transposed) operand read straight from a row-major tile.
+__device__ inline u32x2 lds_read_tr16(const void* p) {
+  typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// max(x, x of lane ^ 32) in every lane, without LDS: permlane32_swap with
+// both operands x leaves [x_lo, x_lo] in the first result and [x_hi, x_hi]
+// in the second.
+__device__ inline float max_with_other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
+__device__ inline bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
 // Workgroups are dispatched round-robin over the 8 XCDs (bid % 8). Remap so
 // that consecutive logical tiles (the query tiles of one head, which read the
 // same K/V) land on the same XCD and share its L2. A bijection on [0, total).

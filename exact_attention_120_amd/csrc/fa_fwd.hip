@@ -46,49 +46,47 @@ struct FwdShape {
   static constexpr int KH = E::KH;
   static constexpr int ES = sizeof(T);
   static constexpr int EPV = 16 / ES;        // elements per 16-byte vector
+  static constexpr bool TRV = ES == 2;       // V read with transposing LDS loads
   static constexpr int DH = D / 2;           // head-dim elements per lane half
   static constexpr int NQK = DH / KH;        // MFMAs per 32x32 score tile
   static constexpr int NMT = kBN / 32;       // 32-key blocks per tile
   static constexpr int NDT = D / 32;         // 32-wide head-dim blocks of O
   static constexpr int NPV = kBN / (2 * KH); // PV MFMAs per head-dim block
-  static constexpr int KS = D + EPV;         // K row stride in LDS (elements)
-  static constexpr int VS = kBN + EPV;       // V^T row stride in LDS (elements)
+  static constexpr int KS = D + EPV;         // K row stride in LDS (elements, +16 B)
+  // V: row-major, unpadded, 16-byte units XOR-swizzled by key (16-bit types);
+  // fp32 keeps a transposed V^T copy (keys contiguous, permuted by vt_pos).
+  static constexpr int VS = TRV ? D : kBN + EPV;
   static constexpr int K_BYTES = kBN * KS * ES;
-  static constexpr int V_BYTES = D * VS * ES;
+  static constexpr int V_BYTES = TRV ? kBN * D * ES : D * VS * ES;
   static constexpr int STAGE = K_BYTES + V_BYTES;
-  static constexpr int K_VECS = kBN * D / EPV / kThreads;   // 16B K loads / thread
-  static constexpr int V_ITEMS = (kBN / 4) * (D / EPV);      // (4 keys x 16B) items
-  static constexpr int V_PER_T = (V_ITEMS + kThreads - 1) / kThreads;
-  static_assert(kBN * D / EPV % kThreads == 0, "K tile must split evenly");
+  static constexpr int VECS = kBN * D / EPV / kThreads;     // 16 B loads per thread per tensor
+  static_assert(kBN * D / EPV % kThreads == 0, "tile must split evenly");
 };
+
+// Swizzle of the 16-byte units of V row `key` (16-bit types). With it, the
+// transposing reads of one wave (8 rows x 64 B) and the row writes (16 B per
+// lane) are free of LDS bank conflicts (measured with SQ_LDS_BANK_CONFLICT).
+template <int D>
+__device__ constexpr int v_swz(int key) {
+  return D == 128 ? (0xCA60 >> (4 * (key & 3))) & 15 : 2 * (key & 3);
+}
 
 template <typename T, int D>
 struct TileLoader {
   using S = FwdShape<T, D>;
-  u32x4 kreg[S::K_VECS];
-  u32x4 vreg[S::V_PER_T][4];
+  u32x4 kreg[S::VECS];
+  u32x4 vreg[S::VECS];
 
-  __device__ inline void load(const T* K, const T* V, int k0, int N, int tid) {
+  // Rows past N read as zeros (buffer range check).
+  __device__ inline void load(const HeadBuf& K, const HeadBuf& V, int k0, int tid) {
 #pragma unroll
-    for (int i = 0; i < S::K_VECS; ++i) {
+    for (int i = 0; i < S::VECS; ++i) {
       const int idx = tid + kThreads * i;
       const int row = idx / (D / S::EPV);
       const int c = (idx % (D / S::EPV)) * S::EPV;
-      const int key = k0 + row;
-      kreg[i] = key < N ? ld<u32x4>(K + (size_t)key * D + c) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < S::V_PER_T; ++i) {
-      const int item = tid + kThreads * i;
-      if (S::V_ITEMS % kThreads == 0 || item < S::V_ITEMS) {
-        const int kg = item / (D / S::EPV);
-        const int c = (item % (D / S::EPV)) * S::EPV;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int key = k0 + 4 * kg + kk;
-          vreg[i][kk] = key < N ? ld<u32x4>(V + (size_t)key * D + c) : u32x4{0, 0, 0, 0};
-        }
-      }
+      const int off = ((k0 + row) * D + c) * S::ES;
+      kreg[i] = K.ld16(off);
+      vreg[i] = V.ld16(off);
     }
   }
 
@@ -96,39 +94,17 @@ struct TileLoader {
     char* Kl = stage;
     char* Vl = stage + S::K_BYTES;
 #pragma unroll
-    for (int i = 0; i < S::K_VECS; ++i) {
+    for (int i = 0; i < S::VECS; ++i) {
       const int idx = tid + kThreads * i;
       const int row = idx / (D / S::EPV);
       const int c = (idx % (D / S::EPV)) * S::EPV;
       st<u32x4>(Kl + (row * S::KS + c) * S::ES, kreg[i]);
-    }
+      if constexpr (S::TRV) {
+        st<u32x4>(Vl + row * D * 2 + (((c >> 3) ^ v_swz<D>(row)) << 4), vreg[i]);
+      } else {
 #pragma unroll
-    for (int i = 0; i < S::V_PER_T; ++i) {
-      const int item = tid + kThreads * i;
-      if (S::V_ITEMS % kThreads == 0 || item < S::V_ITEMS) {
-        const int kg = item / (D / S::EPV);
-        const int c = (item % (D / S::EPV)) * S::EPV;
-        if constexpr (S::ES == 2) {
-          // 4 keys x 8 head-dim elements -> 8 rows of V^T, 4 adjacent keys each.
-          const int pos = vt_pos<S::KH>(4 * kg);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int w = e >> 1, sh = (e & 1) * 16;
-            const uint32_t a0 = (vreg[i][0][w] >> sh) & 0xffffu;
-            const uint32_t a1 = (vreg[i][1][w] >> sh) & 0xffffu;
-            const uint32_t a2 = (vreg[i][2][w] >> sh) & 0xffffu;
-            const uint32_t a3 = (vreg[i][3][w] >> sh) & 0xffffu;
-            st<u32x2>(Vl + ((c + e) * S::VS + pos) * 2, u32x2{a0 | (a1 << 16), a2 | (a3 << 16)});
-          }
-        } else {
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            const int pos = vt_pos<S::KH>(4 * kg + kk);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              st<uint32_t>(Vl + ((c + e) * S::VS + pos) * 4, vreg[i][kk][e]);
-          }
-        }
+        for (int e = 0; e < 4; ++e)
+          st<uint32_t>(Vl + ((c + e) * S::VS + vt_pos<S::KH>(row)) * 4, vreg[i][e]);
       }
     }
   }
@@ -151,9 +127,10 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(F
   const int q0 = qtile * kBM;
 
   const size_t head = (size_t)bh * N * D;
-  const T* Q = reinterpret_cast<const T*>(a.q) + head;
-  const T* K = reinterpret_cast<const T*>(a.k) + head;
-  const T* V = reinterpret_cast<const T*>(a.v) + head;
+  const uint32_t head_bytes = (uint32_t)N * D * S::ES;
+  const HeadBuf Q(reinterpret_cast<const T*>(a.q) + head, head_bytes);
+  const HeadBuf K(reinterpret_cast<const T*>(a.k) + head, head_bytes);
+  const HeadBuf V(reinterpret_cast<const T*>(a.v) + head, head_bytes);
   T* O = reinterpret_cast<T*>(a.o) + head;
   float* L = a.lse + (size_t)bh * N;
 
@@ -168,8 +145,29 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(F
   // [h*D/2, h*D/2 + D/2) of its row, KH per MFMA.
   Raw qf[S::NQK];
 #pragma unroll
-  for (int i = 0; i < S::NQK; ++i)
-    qf[i] = qrow < N ? ld<Raw>(Q + (size_t)qrow * D + half * S::DH + i * KH) : Raw{};
+  for (int i = 0; i < S::NQK; ++i) {
+    const int off = (qrow * D + half * S::DH + i * KH) * S::ES;
+    if constexpr (S::ES == 2)
+      qf[i] = Q.ld16(off);
+    else
+      qf[i] = Q.ld4(off);
+  }
+
+  // Per-lane byte offsets of the V^T operand reads within a stage's V tile.
+  // Transposing reads: lane 4r+q of 16-lane group g fetches key row 4h + r
+  // (h = g/2) and head-dim columns 32*dt + 16*(g&1) + 4q .. +4.
+  int voff[S::NDT];
+  {
+    const int g = lane >> 4, jf = lane & 15, r = jf >> 2, q = jf & 3, h = g >> 1;
+    const int b = 2 * (g & 1) + (q >> 1);  // 16-byte unit within a 32-wide block
+#pragma unroll
+    for (int dt = 0; dt < S::NDT; ++dt) {
+      if constexpr (S::TRV)
+        voff[dt] = (4 * h + r) * D * 2 + (((4 * dt) ^ (b ^ v_swz<D>(r))) << 4) + (q & 1) * 8;
+      else
+        voff[dt] = ((dt * 32 + col) * S::VS + half * KH) * S::ES;
+    }
+  }
 
   // Key tiles this workgroup visits: all of them, or (causal) only those
   // holding a key <= the last query row of the tile.
@@ -177,91 +175,101 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(F
   const int nkv = CAUSAL ? min(nkv_all, (min(q0 + kBM, N) - 1) / kBN + 1) : nkv_all;
 
   const float c = a.scale_log2;  // scale * log2(e)
-  float m = -FLT_MAX;            // running max of raw scores (this row)
-  float l = 0.f;                 // running sum of probabilities (this lane's keys)
+  // Reference max (raw scores) the exponentials are taken against; it only
+  // moves when a row's max exceeds it by more than 2^8 in probability
+  // (exact: O and l are always relative to the same reference).
+  float m = -FLT_MAX;
+  float l = 0.f;  // running sum of probabilities (this lane's keys)
   f32x16 o[S::NDT];
 #pragma unroll
   for (int dt = 0; dt < S::NDT; ++dt) o[dt] = f32x16{};
 
-  TileLoader<T, D> tl;
-  tl.load(K, V, 0, N, tid);
-  tl.store(lds, tid);
-  __syncthreads();
-
-  for (int j = 0; j < nkv; ++j) {
-    const char* stage = lds + (j & 1) * S::STAGE;
-    if (j + 1 < nkv) tl.load(K, V, (j + 1) * kBN, N, tid);
-    const int k0 = j * kBN;
-
-    if (wave_active && (!CAUSAL || k0 <= qw0 + 31)) {
-      // S^T = K Q^T for 64 keys x 32 queries.
-      f32x16 s[S::NMT];
+  auto tile = [&](const char* stage, int k0, bool need_mask) {
+    // S^T = K Q^T for 64 keys x 32 queries.
+    f32x16 s[S::NMT];
 #pragma unroll
-      for (int mt = 0; mt < S::NMT; ++mt) {
-        s[mt] = f32x16{};
-        const char* kp = stage + ((mt * 32 + col) * S::KS + half * S::DH) * S::ES;
+    for (int mt = 0; mt < S::NMT; ++mt) {
+      s[mt] = f32x16{};
+      const char* kp = stage + ((mt * 32 + col) * S::KS + half * S::DH) * S::ES;
 #pragma unroll
-        for (int i = 0; i < S::NQK; ++i) s[mt] = E::mma(ld<Raw>(kp + i * KH * S::ES), qf[i], s[mt]);
-      }
-
-      const bool need_mask = (CAUSAL && k0 + kBN - 1 > qw0) || (k0 + kBN > N);
-      if (need_mask) {
-#pragma unroll
-        for (int mt = 0; mt < S::NMT; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            const bool vis = key < N && (!CAUSAL || key <= qrow);
-            if (!vis) s[mt][r] = -INFINITY;
-          }
-      }
-
-      // Online softmax update (row max over this lane's 32 scores, then the
-      // partner lane half).
-      float mx = -INFINITY;
+      for (int i = 0; i < S::NQK; ++i) s[mt] = E::mma(ld<Raw>(kp + i * KH * S::ES), qf[i], s[mt]);
+    }
+    if (need_mask) {  // diagonal or tail tile: hidden scores -> -inf (probability 0)
 #pragma unroll
       for (int mt = 0; mt < S::NMT; ++mt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m, mx);
-      const float mc = m_new * c;
-      const float alpha = __builtin_amdgcn_exp2f(m * c - mc);
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const bool vis = key < N && (!CAUSAL || key <= qrow);
+          if (!vis) s[mt][r] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < S::NMT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
+    mx = max_with_other_half(mx);
+    const float m_new = fmaxf(m, mx);
+    if (wave_any((m_new - m) * c > 8.f || m == -FLT_MAX)) {
+      const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
       m = m_new;
       l *= alpha;
 #pragma unroll
       for (int dt = 0; dt < S::NDT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    }
+    const float mc = m * c;
 
-      // Probabilities -> MFMA B operands (P^T), in register order.
-      Raw pf[S::NMT * (16 / KH)];
+    // Probabilities -> MFMA B operands (P^T), in register order.
+    Raw pf[S::NMT * (16 / KH)];
 #pragma unroll
-      for (int mt = 0; mt < S::NMT; ++mt)
+    for (int mt = 0; mt < S::NMT; ++mt)
 #pragma unroll
-        for (int u = 0; u < 16 / KH; ++u) {
-          float p[KH];
+      for (int u = 0; u < 16 / KH; ++u) {
+        float p[KH];
 #pragma unroll
-          for (int jj = 0; jj < KH; ++jj) {
-            const float sv = s[mt][u * KH + jj];
-            float t = __builtin_amdgcn_exp2f(fmaf(sv, c, -mc));
-            if (need_mask) t = sv == -INFINITY ? 0.f : t;
-            p[jj] = t;
-          }
-          pf[mt * (16 / KH) + u] = E::pack_sum(p, l);
+        for (int jj = 0; jj < KH; ++jj) {
+          // c > 0 always (the host passes max(scale*log2(e), FLT_MIN)), so
+          // a hidden score (-inf) gives exactly 0.
+          p[jj] = __builtin_amdgcn_exp2f(fmaf(s[mt][u * KH + jj], c, -mc));
         }
+        pf[mt * (16 / KH) + u] = E::pack_sum(p, l);
+      }
 
-      // O^T += V^T P^T.
-      const char* vbase = stage + S::K_BYTES;
+    // O^T += V^T P^T.
+    const char* vbase = stage + S::K_BYTES;
 #pragma unroll
-      for (int dt = 0; dt < S::NDT; ++dt) {
-        const char* vp = vbase + ((dt * 32 + col) * S::VS + half * KH) * S::ES;
+    for (int dt = 0; dt < S::NDT; ++dt) {
+      const char* vp = vbase + voff[dt];
 #pragma unroll
-        for (int u = 0; u < S::NPV; ++u)
-          o[dt] = E::mma(ld<Raw>(vp + u * 2 * KH * S::ES), pf[u], o[dt]);
+      for (int u = 0; u < S::NPV; ++u) {
+        Raw va;
+        if constexpr (S::TRV) {
+          const u32x2 lo = lds_read_tr16(vp + (16 * u) * D * 2);
+          const u32x2 hi = lds_read_tr16(vp + (16 * u + 8) * D * 2);
+          va = Raw{lo[0], lo[1], hi[0], hi[1]};
+        } else {
+          va = ld<Raw>(vp + u * 2 * KH * S::ES);
+        }
+        o[dt] = E::mma(va, pf[u], o[dt]);
       }
     }
+  };
 
+  TileLoader<T, D> tl;
+  tl.load(K, V, 0, tid);
+  tl.store(lds, tid);
+  __syncthreads();
+
+  for (int j = 0; j < nkv; ++j) {
+    const char* stage = lds + (j & 1) * S::STAGE;
+    if (j + 1 < nkv) tl.load(K, V, (j + 1) * kBN, tid);
+    const int k0 = j * kBN;
+    if (wave_active && (!CAUSAL || k0 <= qw0 + 31)) {
+      tile(stage, k0, (CAUSAL && k0 + kBN - 1 > qw0) || (k0 + kBN > N));
+    }
     if (j + 1 < nkv) tl.store(lds + ((j + 1) & 1) * S::STAGE, tid);
     __syncthreads();
   }
