@@ -59,6 +59,12 @@ struct Elem<__bf16> {
     }
     return r;
   }
+  // One pair of pack_sum: the packed word of (a, b); acc += a + b.
+  __device__ static inline uint32_t pack2(float a, float b, float& acc) {
+    const bf16x2 pr = {(__bf16)a, (__bf16)b};
+    acc += a + b;
+    return __builtin_bit_cast(uint32_t, pr);
+  }
   __device__ static inline uint16_t bits(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
   }
@@ -85,6 +91,12 @@ struct Elem<_Float16> {
       r[w] = __builtin_bit_cast(uint32_t, pr);
     }
     return r;
+  }
+  __device__ static inline uint32_t pack2(float a, float b, float& acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    const f16x2 pr = {(_Float16)a, (_Float16)b};
+    acc = __builtin_amdgcn_fdot2(pr, one, acc, false);
+    return __builtin_bit_cast(uint32_t, pr);
   }
   __device__ static inline uint16_t bits(float x) {
     return __builtin_bit_cast(uint16_t, (_Float16)x);
@@ -139,6 +151,10 @@ struct HeadBuf {
   __device__ inline u32x4 ld16(int byte_off) const {
     return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
   }
+  // Per-lane offset plus a wave-uniform one (kept in a scalar register).
+  __device__ inline u32x4 ld16(int byte_off, int uniform_off) const {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, uniform_off, 0);
+  }
   __device__ inline uint32_t ld4(int byte_off) const {
     return __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0);
   }
@@ -164,6 +180,17 @@ __device__ inline float max_with_other_half(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
                                                   __builtin_bit_cast(uint32_t, x), false, false);
   return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
+// An empty asm statement that reads `x`: the compiler must complete any load
+// into `x` before this point. Used after a kernel's prologue so that no load
+// is still pending when its main loop starts; otherwise the wait-count
+// insertion, which merges loop-entry and back-edge states, waits on that
+// load inside every iteration, and thereby also on the next tile's
+// prefetch loads issued after it.
+template <typename X>
+__device__ inline void settle(const X& x) {
+  asm volatile("" ::"v"(x));
 }
 
 __device__ inline bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }

@@ -9,23 +9,33 @@
 // dimension and key/value blocks in the inner loop, blocks above the causal
 // diagonal never visited, and only O plus the normalizer written to HBM.
 //
-// gfx950 design (one workgroup = 4 waves = 128 query rows of one head):
-//   * grid: B*H*ceil(N/128) workgroups, remapped so the query tiles of a head
+// gfx950 design, 16-bit inputs (bf16, fp16): one workgroup = 8 waves = 256
+// query rows of one head, in two groups of four waves (A = waves 0-3,
+// B = waves 4-7; wave w runs on SIMD w % 4, so each SIMD holds one wave of
+// each group).
+//   * grid: B*H*ceil(N/256) workgroups, remapped so the query tiles of a head
 //     share one XCD's L2; causal grids run the longest rows first.
 //   * each wave owns 32 query rows; its Q tile stays in registers as MFMA B
 //     operands for the whole key loop.
-//   * per 64-key tile, K is staged in LDS row-major and V transposed (V^T,
-//     keys contiguous, permuted to the order in which the score registers
-//     feed the PV product), both double-buffered and padded by 16 bytes per
-//     row against bank conflicts; the next tile's global loads are in flight
-//     while the current tile computes.
-//   * S^T = K Q^T on MFMA 32x32x16 (bf16/fp16) or 32x32x2 (fp32): each lane
-//     then holds 16 scores of a single query row, so the row max is lane-local
-//     plus one exchange with lane^32, and the probabilities feed O^T += V^T P^T
-//     straight from registers with no LDS round trip.
+//   * work per 64-key tile i is split into a matrix phase M(i) -- O += P V
+//     for tile i-1, then S^T = K Q^T for tile i -- and a vector phase V(i),
+//     the online softmax of tile i. Phases end at workgroup barriers and
+//     group B runs one phase behind group A, so on every SIMD one wave's
+//     MFMA phase overlaps the other wave's softmax ("ping-pong").
+//   * K and V tiles (64 keys) are double-buffered in LDS, K row-major padded
+//     by 16 bytes per row, V row-major with its 16-byte units XOR-swizzled by
+//     key and read transposed (ds_read_b64_tr_b16) as the V^T operand. Global
+//     loads are issued in a wave's matrix phase into registers and written to
+//     LDS in its vector phase: group A streams V tile i, group B K tile i+2.
+//   * S^T = K Q^T leaves each lane 16 scores of a single query row, so the
+//     row max is lane-local plus one exchange with lane^32, and P^T feeds
+//     O^T += V^T P^T straight from registers with no LDS round trip.
 //   * softmax in float32 with exp2 and scale*log2(e) folded into one FMA per
 //     score, tracking the raw-score max (valid because scale >= 0); 1/l is
 //     applied once in the epilogue (the FA2 reduction of non-matmul work).
+//
+// float32 inputs use a plainer kernel (4 waves = 128 rows per workgroup, one
+// loop doing all three steps per tile) on the 32x32x2 fp32 MFMA.
 #include <float.h>
 
 #include "fa_device.hpp"
@@ -261,6 +271,8 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(F
   TileLoader<T, D> tl;
   tl.load(K, V, 0, tid);
   tl.store(lds, tid);
+#pragma unroll
+  for (int i = 0; i < S::NQK; ++i) settle(qf[i]);
   __syncthreads();
 
   for (int j = 0; j < nkv; ++j) {
@@ -295,14 +307,334 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(F
   if (half == 0) L[qrow] = m * a.scale + logf(lt);
 }
 
+// ---------------------------------------------------------------------------
+// 16-bit kernel: 8 waves, ping-pong between matrix and vector phases.
+
+constexpr int kPPWaves = 8;
+constexpr int kPPThreads = kPPWaves * 64;
+constexpr int kPPGroup = kPPThreads / 2;  // threads per wave group
+constexpr int kPPBM = kPPWaves * 32;      // query rows per workgroup
+
+template <typename T, int D>
+struct PPShape {
+  static constexpr int KH = 8;               // operand elements per lane per MFMA
+  static constexpr int NQK = D / 2 / KH;     // MFMAs per 32x32 score tile
+  static constexpr int NMT = kBN / 32;       // 32-key blocks per tile
+  static constexpr int NDT = D / 32;         // 32-wide head-dim blocks of O
+  static constexpr int NPV = kBN / 16;       // PV MFMAs per head-dim block
+  static constexpr int NPF = NMT * 2;        // P^T operands per tile
+  static constexpr int KS = D + 8;           // K row stride in LDS (elements, +16 B)
+  static constexpr int K_BYTES = kBN * KS * 2;
+  static constexpr int V_BYTES = kBN * D * 2;
+  static constexpr int LDS_BYTES = 2 * K_BYTES + 2 * V_BYTES;
+  static constexpr int VECS = kBN * D / 8 / kPPGroup;  // 16 B per thread per tile
+  static_assert(kBN * D / 8 % kPPGroup == 0, "tile must split evenly over a group");
+};
+
+// One wave group's share of a 64-key tile, staged in registers between the
+// global load (matrix phase) and the LDS store (vector phase). Vector i of a
+// thread is tile row ROWS*i + gtid/(D/8), columns 8*(gtid % (D/8)) .. +8, so
+// the global offsets are contiguous and the LDS offsets step by a constant.
+template <int D>
+struct GroupStage {
+  static constexpr int VECS = PPShape<__bf16, D>::VECS;
+  static constexpr int ROWS = kPPGroup / (D / 8);  // tile rows per vector step
+  static constexpr int K_STRIDE = ROWS * (D + 8) * 2;
+  static constexpr int V_STRIDE = ROWS * D * 2;
+  u32x4 r[VECS];
+
+  // Rows past N read as zeros (buffer range check).
+  __device__ inline void load(const HeadBuf& X, int k0, int gtid) {
+#pragma unroll
+    for (int i = 0; i < VECS; ++i) r[i] = X.ld16((gtid + kPPGroup * i) * 16, k0 * D * 2);
+  }
+  __device__ inline void store(char* dst, int off0, int stride) const {
+#pragma unroll
+    for (int i = 0; i < VECS; ++i) st<u32x4>(dst + off0 + i * stride, r[i]);
+  }
+  // LDS byte offset of vector 0: K row-major with rows padded by 16 bytes;
+  // V row-major with 16-byte units XOR-swizzled by key.
+  __device__ static inline int k_off(int gtid) {
+    const int row = gtid / (D / 8), c = (gtid % (D / 8)) * 8;
+    return (row * (D + 8) + c) * 2;
+  }
+  __device__ static inline int v_off(int gtid) {
+    const int row = gtid / (D / 8), c = (gtid % (D / 8)) * 8;
+    return row * D * 2 + (((c >> 3) ^ v_swz<D>(row)) << 4);
+  }
+};
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a) {
+  using S = PPShape<T, D>;
+  using E = Elem<T>;
+  using Raw = typename E::Raw;
+  constexpr int KH = S::KH;
+
+  __shared__ __attribute__((aligned(16))) char lds[S::LDS_BYTES];
+  char* const kbuf = lds;                     // 2 x K tile
+  char* const vbuf = lds + 2 * S::K_BYTES;    // 2 x V tile
+
+  const int N = a.N;
+  const int nqt = (N + kPPBM - 1) / kPPBM;
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = lin / nqt;
+  const int qtile = CAUSAL ? nqt - 1 - lin % nqt : lin % nqt;
+  const int q0 = qtile * kPPBM;
+
+  const size_t head = (size_t)bh * N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const HeadBuf Q(reinterpret_cast<const T*>(a.q) + head, head_bytes);
+  const HeadBuf K(reinterpret_cast<const T*>(a.k) + head, head_bytes);
+  const HeadBuf V(reinterpret_cast<const T*>(a.v) + head, head_bytes);
+  T* O = reinterpret_cast<T*>(a.o) + head;
+  float* L = a.lse + (size_t)bh * N;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int group = wave >> 2;         // 0: A, 1: B (one phase behind)
+  const int gtid = tid & (kPPGroup - 1);
+  const int col = lane & 31, half = lane >> 5;
+  const int qw0 = q0 + wave * 32;      // first query row of this wave
+  const int qrow = qw0 + col;          // the query row this lane serves
+
+  // Key tiles: the workgroup streams those any of its rows can see; this
+  // wave computes on those its own rows can see.
+  const int nkv_all = (N + kBN - 1) / kBN;
+  const int nkv = CAUSAL ? min(nkv_all, (min(q0 + kPPBM, N) - 1) / kBN + 1) : nkv_all;
+  const int nkv_w = qw0 >= N ? 0 : CAUSAL ? min(nkv_all, (qw0 + 31) / kBN + 1) : nkv_all;
+
+  // Q^T as MFMA B operands: lane half h holds head-dim elements
+  // [h*D/2, h*D/2 + D/2) of its row, KH per MFMA.
+  Raw qf[S::NQK];
+#pragma unroll
+  for (int i = 0; i < S::NQK; ++i) qf[i] = Q.ld16((qrow * D + half * (D / 2) + i * KH) * 2);
+
+  // Per-lane byte offsets of the transposing V^T operand reads: lane 4r+q of
+  // 16-lane group g fetches key row 4h + r (h = g/2) and head-dim columns
+  // 32*dt + 16*(g&1) + 4q .. +4.
+  int voff[S::NDT];
+  {
+    const int g = lane >> 4, jf = lane & 15, r = jf >> 2, q = jf & 3, h = g >> 1;
+    const int b = 2 * (g & 1) + (q >> 1);
+#pragma unroll
+    for (int dt = 0; dt < S::NDT; ++dt)
+      voff[dt] = (4 * h + r) * D * 2 + (((4 * dt) ^ (b ^ v_swz<D>(r))) << 4) + (q & 1) * 8;
+  }
+  const int koff = (col * S::KS + half * (D / 2)) * 2;
+
+  const float c = a.scale_log2;  // scale * log2(e)
+  // Reference max (raw scores) the exponentials are taken against; it only
+  // moves when a row's max exceeds it by more than 2^8 in probability
+  // (exact: O and l are always relative to the same reference).
+  float m = -FLT_MAX;
+  float l = 0.f;  // running sum of probabilities (this lane's keys)
+  f32x16 o[S::NDT];
+#pragma unroll
+  for (int dt = 0; dt < S::NDT; ++dt) o[dt] = f32x16{};
+  // Scores of a tile (from its matrix phase to its vector phase), then its
+  // packed probabilities (to the next matrix phase): never live together, so
+  // they share registers -- P^T operand k lives in words [4k, 4k+4) of s.
+  // (Operands are taken out with constant-index shuffles: rebuilding a
+  // vector element by element from another vector's elements mis-compiles.)
+  f32x16 s[S::NMT];
+#pragma unroll
+  for (int mt = 0; mt < S::NMT; ++mt) s[mt] = f32x16{};
+  static_assert(S::NPF == 4, "P^T operands of a 64-key tile fill s[0]");
+
+  // Matrix phase: O^T += V^T P^T for the previous tile (PV), then
+  // S^T = K Q^T for the current one (QK). The MFMAs run in chunks of four;
+  // the LDS operands of chunk c + 1 are read while chunk c computes, so the
+  // phase hides its own LDS latency (the other wave on this SIMD is in its
+  // vector phase and issues no MFMAs to fill the gaps). PV chunk dt covers
+  // head-dim block dt; QK chunk (mt, h) covers key block mt and head-dim
+  // operands 4h .. 4h + 3. The P^T operands sit in s[0] and are consumed by
+  // the PV chunks before the QK chunks overwrite s.
+  auto mphase = [&](const char* vt, const char* kt, auto pv_c, auto qk_c) {
+    constexpr bool PV = decltype(pv_c)::value, QK = decltype(qk_c)::value;
+    constexpr int QKH = S::NQK / 4;  // QK chunks per key block
+    constexpr int NPVC = PV ? S::NDT : 0;
+    constexpr int NC = NPVC + (QK ? S::NMT * QKH : 0);
+    const f32x16 x = s[0];
+    const Raw pf[4] = {
+        __builtin_bit_cast(Raw, __builtin_shufflevector(x, x, 0, 1, 2, 3)),
+        __builtin_bit_cast(Raw, __builtin_shufflevector(x, x, 4, 5, 6, 7)),
+        __builtin_bit_cast(Raw, __builtin_shufflevector(x, x, 8, 9, 10, 11)),
+        __builtin_bit_cast(Raw, __builtin_shufflevector(x, x, 12, 13, 14, 15))};
+    Raw op[2][4];
+    auto fetch = [&](int c, Raw(&dst)[4]) {
+      if (c < NPVC) {
+        const char* vp = vt + voff[c];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const u32x2 lo = lds_read_tr16(vp + (16 * u) * D * 2);
+          const u32x2 hi = lds_read_tr16(vp + (16 * u + 8) * D * 2);
+          dst[u] = Raw{lo[0], lo[1], hi[0], hi[1]};
+        }
+      } else {
+        const int mt = (c - NPVC) / QKH, h = (c - NPVC) % QKH;
+        const char* kp = kt + koff + mt * 32 * S::KS * 2 + h * 4 * KH * 2;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dst[j] = ld<Raw>(kp + j * KH * 2);
+      }
+    };
+    auto compute = [&](int c, const Raw(&src)[4]) {
+      if (c < NPVC) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) o[c] = E::mma(src[u], pf[u], o[c]);
+      } else {
+        const int mt = (c - NPVC) / QKH, h = (c - NPVC) % QKH;
+        if (h == 0) s[mt] = f32x16{};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s[mt] = E::mma(src[j], qf[h * 4 + j], s[mt]);
+      }
+    };
+    static_assert(S::NPV == 4 && S::NQK % 4 == 0, "chunks of four MFMAs");
+    __builtin_amdgcn_s_setprio(1);
+    fetch(0, op[0]);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (c + 1 < NC) fetch(c + 1, op[(c + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(c, op[c & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // Online softmax of one tile: scores s -> probabilities pf.
+  auto softmax = [&](int k0) {
+    if ((CAUSAL && k0 + kBN - 1 > qw0) || k0 + kBN > N) {
+      // Diagonal or tail tile: hidden scores -> -inf (probability 0).
+#pragma unroll
+      for (int mt = 0; mt < S::NMT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const bool vis = key < N && (!CAUSAL || key <= qrow);
+          if (!vis) s[mt][r] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < S::NMT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
+    mx = max_with_other_half(mx);
+    const float m_new = fmaxf(m, mx);
+    if (wave_any((m_new - m) * c > 8.f || m == -FLT_MAX)) {
+      const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < S::NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    }
+    const float mc = m * c;
+    // Operand k = 2*mt + u packs scores s[mt][8u .. 8u+8) and is written to
+    // words [4k, 4k+4) of s, all of which were read by earlier operands.
+    // Each packed pair goes straight to its word: reading words back out of
+    // a vector assembled from packed 16-bit pairs mis-compiles.
+#pragma unroll
+    for (int mt = 0; mt < S::NMT; ++mt)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float p[KH];
+#pragma unroll
+        for (int jj = 0; jj < KH; ++jj) {
+          // c > 0 always (the host passes max(scale*log2(e), FLT_MIN)), so
+          // a hidden score (-inf) gives exactly 0.
+          p[jj] = __builtin_amdgcn_exp2f(fmaf(s[mt][u * KH + jj], c, -mc));
+        }
+        const int k = mt * 2 + u;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          s[k / 4][(k % 4) * 4 + w] = __builtin_bit_cast(float, E::pack2(p[2 * w], p[2 * w + 1], l));
+      }
+  };
+
+  // Prologue: K tiles 0 and 1 (group A stages tile 0, group B tile 1).
+  using GS = GroupStage<D>;
+  GS stg;
+  if (group == 0 || nkv > 1) {
+    stg.load(K, group * kBN, gtid);
+    stg.store(kbuf + group * S::K_BYTES, GS::k_off(gtid), GS::K_STRIDE);
+  }
+#pragma unroll
+  for (int i = 0; i < S::NQK; ++i) settle(qf[i]);
+  __syncthreads();
+
+  // Step i is a matrix phase M(i) then a vector phase V(i), each ending at a
+  // barrier; group B runs one phase behind group A (one extra barrier first,
+  // A one extra at the end), so the phases of the two groups alternate.
+  // Group A streams V tile i (global load in M(i), LDS store in V(i)), group
+  // B K tile i + 2. K tile i lives in kbuf[i % 2] and V tile i in vbuf[i % 2];
+  // each store lands in a buffer whose last readers passed an earlier barrier.
+  const bool kgrp = group == 1;
+  const HeadBuf& X = kgrp ? K : V;
+  const int soff = kgrp ? GS::k_off(gtid) : GS::v_off(gtid);
+  const int sstride = kgrp ? GS::K_STRIDE : GS::V_STRIDE;
+  if (kgrp) __syncthreads();
+  // Step 0 (no PV yet).
+  {
+    const int lt = kgrp ? 2 : 0;
+    if (lt < nkv) stg.load(X, lt * kBN, gtid);
+    if (nkv_w > 0) mphase(vbuf, kbuf, BoolC<false>{}, BoolC<true>{});
+    __syncthreads();
+    if (nkv_w > 0) softmax(0);
+    if (lt < nkv) stg.store(kgrp ? kbuf : vbuf, soff, sstride);
+    __syncthreads();
+  }
+  // Steps 1 .. nkv-1, one code path: at step nkv_w (a causal wave past its
+  // last visible tile) only the PV half matters and the QK half is unused.
+  for (int i = 1; i < nkv; ++i) {
+    const int lt = kgrp ? i + 2 : i;  // the tile this group streams
+    if (lt < nkv) stg.load(X, lt * kBN, gtid);
+    if (i <= nkv_w)
+      mphase(vbuf + ((i - 1) & 1) * S::V_BYTES, kbuf + (i & 1) * S::K_BYTES, BoolC<true>{},
+             BoolC<true>{});
+    __syncthreads();
+    if (i < nkv_w) softmax(i * kBN);
+    if (lt < nkv) stg.store(kgrp ? kbuf + (i & 1) * S::K_BYTES : vbuf + (i & 1) * S::V_BYTES, soff, sstride);
+    __syncthreads();
+  }
+  // Final matrix phase: PV of the last tile.
+  if (nkv == nkv_w) mphase(vbuf + ((nkv - 1) & 1) * S::V_BYTES, kbuf, BoolC<true>{}, BoolC<false>{});
+  __syncthreads();
+  if (!kgrp) __syncthreads();
+
+  if (nkv_w == 0 || qrow >= N) return;
+  const float lt = l + __shfl_xor(l, 32);
+  const float inv = 1.0f / lt;
+  T* orow = O + (size_t)qrow * D;
+#pragma unroll
+  for (int dt = 0; dt < S::NDT; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = dt * 32 + 8 * g + 4 * half;
+      const uint32_t w0 = E::bits(o[dt][4 * g] * inv) | ((uint32_t)E::bits(o[dt][4 * g + 1] * inv) << 16);
+      const uint32_t w1 = E::bits(o[dt][4 * g + 2] * inv) | ((uint32_t)E::bits(o[dt][4 * g + 3] * inv) << 16);
+      st<u32x2>(orow + d0, u32x2{w0, w1});
+    }
+  if (half == 0) L[qrow] = m * a.scale + logf(lt);
+}
+
 template <typename T, int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
-  const int nqt = (a.N + kBM - 1) / kBM;
+  constexpr bool kPP = sizeof(T) == 2;
+  const int bm = kPP ? kPPBM : kBM;
+  const int nqt = (a.N + bm - 1) / bm;
   const dim3 grid((unsigned)((long long)a.B * a.H * nqt));
   FwdArgs args = a;
   void* kargs[] = {&args};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_kernel<T, D, CAUSAL>), grid,
-                         dim3(kThreads), kargs, 0, stream);
+  const void* fn;
+  if constexpr (kPP)
+    fn = reinterpret_cast<const void*>(&fwd_pp_kernel<T, D, CAUSAL>);
+  else
+    fn = reinterpret_cast<const void*>(&fwd_kernel<T, D, CAUSAL>);
+  return hipLaunchKernel(fn, grid, dim3(kPP ? kPPThreads : kThreads), kargs, 0, stream);
 }
 
 template <typename T>
