@@ -28,6 +28,14 @@ COMMON = [
 ]
 
 
+# Per-translation-unit flags. The backward kernels keep their MFMA-only
+# operands in AGPRs (pinned in the source) and want every MFMA result in
+# VGPRs, where the vector ALU reads the recomputed scores.
+FILE_FLAGS = {
+    "fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -43,7 +51,7 @@ def sources() -> list[str]:
 def _compile(src: str, extra: list[str]) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [hipcc()] + COMMON + extra + lang + ["-c", src, "-o", obj]
+    cmd = [hipcc()] + COMMON + FILE_FLAGS.get(os.path.basename(src), []) + extra + lang + ["-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stderr}")

@@ -374,6 +374,319 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// 16-bit (bf16, fp16) main kernel.
+//
+// Same decomposition as above (one workgroup = 4 waves x 32 keys, query
+// steps of 64 rows as the inner loop, dK^T and dV^T in registers, dQ through
+// float32 atomics), laid out for gfx950's LDS:
+//   * Q and dO tiles are stored once, row-major, with their 16-byte units
+//     XOR-swizzled by row (tile_off). The swizzle makes both access patterns
+//     free of bank conflicts: 16-byte row reads (the A operands of S = Q K^T
+//     and dP = dO V^T) and transposing 8-byte reads (ds_read_b64_tr_b16, the
+//     Q^T and dO^T operands of dK^T += Q^T dS and dV^T += dO^T P).
+//   * dS goes to LDS as [key][query] with 8-byte stores and comes back
+//     transposed (lane = query) as the A operand of dQ = dS K.
+//   * K^T operands for dQ are read once, transposed, from a swizzled K tile.
+//   * one wave per SIMD: K/V operands (64 registers), dK^T/dV^T (128) and
+//     K^T (32) stay in registers for the whole loop.
+
+constexpr int kStepQ = 64;  // query rows per inner step
+
+// Keeps an MFMA source operand in the accumulation registers (AGPRs), which
+// MFMA instructions read directly: operands that only ever feed MFMAs then
+// leave the VGPR budget to the values the vector ALU works on.
+__device__ inline void pin_acc(u32x4& x) { asm volatile("" : "+a"(x)); }
+
+// XOR swizzle of the 16-byte units of a tile row (ROWB bytes per row, 256 or
+// 128). Conflict-free for 16 lanes reading 16 bytes from 16 consecutive rows
+// (a bijection on row mod 16 over the units of a 256-byte bank line), and
+// for 16 lanes reading 4 consecutive 4-aligned rows x 32 bytes (the four
+// rows' unit pairs land on disjoint banks).
+template <int ROWB>
+__device__ constexpr int row_swz(int row) {
+  if constexpr (ROWB == 256) {
+    return ((row & 3) << 1) | ((row >> 2) & 1) | (((row >> 3) & 1) << 3);
+  } else {
+    const int m = row >> 1;  // two 128-byte rows share a bank line
+    return ((m & 1) << 1) | ((m >> 1) & 1) | (m & 4);
+  }
+}
+
+// Byte offset of `byte` (within its row) of row `row` in a swizzled tile.
+template <int ROWB>
+__device__ constexpr int tile_off(int row, int byte) {
+  return row * ROWB + (((byte >> 4) ^ row_swz<ROWB>(row)) << 4) + (byte & 15);
+}
+
+// Transposed 16-bit MFMA operand from a swizzled row-major tile: lane
+// (c = lane & 31, h = lane >> 5) receives column col0 + c of 8 rows, as
+// the K elements of a 32x32x16 operand. NATURAL: rows row0 + 8h + 0..7;
+// otherwise the order in which a 32x32 C tile's registers hand rows to the
+// next product: row0 + 4h + 0..3, then row0 + 8 + 4h + 0..3.
+template <int ROWB, bool NATURAL>
+__device__ inline u32x4 tr_operand(const char* tile, int row0, int col0, int lane) {
+  const int g = lane >> 4, r = (lane >> 2) & 3, q = lane & 3, h = g >> 1;
+  const int col = col0 + 16 * (g & 1) + 4 * q;
+  const int ra = NATURAL ? row0 + 8 * h + r : row0 + 4 * h + r;
+  const int rb = NATURAL ? ra + 4 : ra + 8;
+  const u32x2 lo = lds_read_tr16(tile + tile_off<ROWB>(ra, col * 2));
+  const u32x2 hi = lds_read_tr16(tile + tile_off<ROWB>(rb, col * 2));
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+template <int D>
+struct Bwd16Shape {
+  static constexpr int ROWB = D * 2;                 // Q / dO / K tile row bytes
+  static constexpr int TILE = kStepQ * ROWB;
+  static constexpr int OFF_DO = TILE;
+  static constexpr int OFF_LSE = 2 * TILE;           // LSE * log2(e), float32
+  static constexpr int OFF_DSUM = 2 * TILE + kStepQ * 4;
+  static constexpr int STAGE = 2 * TILE + 2 * kStepQ * 4;
+  static constexpr int DS_ROWB = kStepQ * 2;         // dS [key][query]
+  static constexpr int LDS = 2 * STAGE + kBN * DS_ROWB;
+  static constexpr int UNITS = D / 8;                // 16-byte units per row
+  static constexpr int NLD = kStepQ * UNITS / kThreads;
+  static constexpr int NKLD = kBN * UNITS / kThreads;
+  static constexpr int NQK = D / 16;                 // MFMAs over the head dim
+  static constexpr int NDT = D / 32;                 // 32-wide head-dim blocks
+  static constexpr int NP = kStepQ / 16;             // P / dS operands per step
+  static constexpr int NKT = kBN / 16;               // K^T operands (dQ product)
+  static constexpr int DQ_UNITS = 2 * NDT / 4;       // (query block, head-dim block) per wave
+  static_assert(NLD * kThreads == kStepQ * UNITS && NKLD * kThreads == kBN * UNITS, "even split");
+  static_assert(kBN * ROWB <= 2 * STAGE, "the K tile is staged in the stage buffers");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void bwd16_kernel(BwdArgs a) {
+  using S = Bwd16Shape<D>;
+  using E = Elem<T>;
+  using Raw = u32x4;
+  constexpr int ROWB = S::ROWB;
+
+  __shared__ __attribute__((aligned(16))) char lds[S::LDS];
+  char* const dsl = lds + 2 * S::STAGE;
+
+  const int N = a.N;
+  const int nkt = (N + kBN - 1) / kBN;
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = lin / nkt;
+  const int k0 = (lin % nkt) * kBN;
+
+  const size_t head = (size_t)bh * N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const HeadBuf Q(reinterpret_cast<const T*>(a.q) + head, head_bytes);
+  const HeadBuf K(reinterpret_cast<const T*>(a.k) + head, head_bytes);
+  const HeadBuf V(reinterpret_cast<const T*>(a.v) + head, head_bytes);
+  const HeadBuf G(reinterpret_cast<const T*>(a.dout) + head, head_bytes);
+  T* dK = reinterpret_cast<T*>(a.dk) + head;
+  T* dV = reinterpret_cast<T*>(a.dv) + head;
+  float* dQacc = a.dq_acc + head;
+  const float* lse = a.lse + (size_t)bh * N;
+  const float* dsum = a.dsum + (size_t)bh * N;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int kw0 = k0 + wave * 32;  // first key of this wave
+  const int key = kw0 + col;       // the key this lane serves in S and dP
+
+  // This wave's K and V rows as B operands over the head dim (rows past N
+  // read as zeros): lane half h holds elements [h*D/2 + 8i, +8) for MFMA i.
+  Raw kb[S::NQK], vb[S::NQK];
+#pragma unroll
+  for (int i = 0; i < S::NQK; ++i) {
+    const int off = (key * D + half * (D / 2) + i * 8) * 2;
+    kb[i] = K.ld16(off);
+    vb[i] = V.ld16(off);
+    pin_acc(kb[i]);
+    pin_acc(vb[i]);
+  }
+
+  // The workgroup's K tile (swizzled) through the stage buffers, then each
+  // wave keeps, as B operands of dQ = dS K, K^T for the head-dim block it
+  // reduces dQ over (natural key order).
+#pragma unroll
+  for (int j = 0; j < S::NKLD; ++j) {
+    const int idx = tid + kThreads * j, row = idx / S::UNITS, u = idx % S::UNITS;
+    st<u32x4>(lds + tile_off<ROWB>(row, u * 16), K.ld16(((k0 + row) * D + u * 8) * 2));
+  }
+  __syncthreads();
+  const int dblk = wave % S::NDT;
+  const int qb0 = wave / S::NDT;  // first query block of this wave's dQ units
+  Raw kq[S::NKT];
+#pragma unroll
+  for (int t = 0; t < S::NKT; ++t) {
+    kq[t] = tr_operand<ROWB, true>(lds, 16 * t, 32 * dblk, lane);
+    pin_acc(kq[t]);
+  }
+  __syncthreads();
+
+  // Per-lane byte offsets of the 16-byte A-operand reads of S and dP: row
+  // `col` (plus 32 per query block), unit h*D/16 + i.
+  int aoff[S::NQK];
+#pragma unroll
+  for (int i = 0; i < S::NQK; ++i) aoff[i] = tile_off<ROWB>(col, (half * (D / 2) + 8 * i) * 2);
+
+  const int nq = (N + kStepQ - 1) / kStepQ;
+  const int it0 = CAUSAL ? k0 / kStepQ : 0;  // first step reaching these keys
+  const float c = a.scale_log2;
+
+  f32x16 dkt[S::NDT], dvt[S::NDT];
+#pragma unroll
+  for (int dt = 0; dt < S::NDT; ++dt) {
+    dkt[dt] = f32x16{};
+    dvt[dt] = f32x16{};
+  }
+
+  // Next step's Q and dO units and one LSE or D value, staged in registers.
+  u32x4 sq[S::NLD], sg[S::NLD];
+  float stat = 0.f;
+  auto load = [&](int q0) {
+#pragma unroll
+    for (int j = 0; j < S::NLD; ++j) {
+      const int idx = tid + kThreads * j, row = idx / S::UNITS, u = idx % S::UNITS;
+      const int off = ((q0 + row) * D + u * 8) * 2;
+      sq[j] = Q.ld16(off);
+      sg[j] = G.ld16(off);
+    }
+    // Threads [0, 64) fetch LSE, [64, 128) D. Rows past N get LSE = +inf
+    // so their probabilities are exactly 0.
+    if (tid < kStepQ) {
+      const int row = q0 + tid;
+      stat = row < N ? lse[row] * kLog2e : INFINITY;
+    } else if (tid < 2 * kStepQ) {
+      const int row = q0 + tid - kStepQ;
+      stat = row < N ? dsum[row] : 0.f;
+    }
+  };
+  auto store = [&](char* stage) {
+#pragma unroll
+    for (int j = 0; j < S::NLD; ++j) {
+      const int idx = tid + kThreads * j, row = idx / S::UNITS, u = idx % S::UNITS;
+      st<u32x4>(stage + tile_off<ROWB>(row, u * 16), sq[j]);
+      st<u32x4>(stage + S::OFF_DO + tile_off<ROWB>(row, u * 16), sg[j]);
+    }
+    if (tid < 2 * kStepQ) st<float>(stage + S::OFF_LSE + tid * 4, stat);
+  };
+
+  load(it0 * kStepQ);
+  store(lds);
+  __syncthreads();
+
+  for (int it = it0; it < nq; ++it) {
+    const char* stage = lds + ((it - it0) & 1) * S::STAGE;
+    const int q0 = it * kStepQ;
+    if (it + 1 < nq) load(q0 + kStepQ);
+
+    // Per 32-query block: S = Q K^T and dP = dO V^T (lane = key, registers
+    // = queries); P = exp2(S*scale*log2e - LSE*log2e) and dS = P * (dP - D),
+    // packed as B operands (P^T, dS^T over the step's queries); dS also goes
+    // to LDS. Operand p = 2*qb + u covers registers [8u, 8u+8) of block qb,
+    // i.e. queries 16p + 4h + 0..3 and 16p + 8 + 4h + 0..3.
+    const bool need_mask = (CAUSAL && q0 < kw0 + 31) || kw0 + 31 >= N;
+    Raw pf[S::NP], sf[S::NP];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int i = 0; i < S::NQK; ++i) {
+        s = E::mma(ld<Raw>(stage + aoff[i] + 32 * qb * ROWB), kb[i], s);
+        dp = E::mma(ld<Raw>(stage + S::OFF_DO + aoff[i] + 32 * qb * ROWB), vb[i], dp);
+      }
+      if (need_mask) {  // hidden scores -> -inf (probability exactly 0)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qrow = q0 + 32 * qb + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (key >= N || (CAUSAL && key > qrow)) s[r] = -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        uint32_t pw[4], sw[4];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int ql = 32 * qb + 16 * u + 8 * k + 4 * half;  // first of 4 query rows
+          const f32x4 l2 = ld<f32x4>(stage + S::OFF_LSE + ql * 4);
+          const f32x4 dd = ld<f32x4>(stage + S::OFF_DSUM + ql * 4);
+          float pe[4], de[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 8 * u + 4 * k + e;
+            pe[e] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -l2[e]));
+            de[e] = pe[e] * (dp[r] - dd[e]);
+          }
+          float unused = 0.f;
+          pw[2 * k] = E::pack2(pe[0], pe[1], unused);
+          pw[2 * k + 1] = E::pack2(pe[2], pe[3], unused);
+          sw[2 * k] = E::pack2(de[0], de[1], unused);
+          sw[2 * k + 1] = E::pack2(de[2], de[3], unused);
+          st<u32x2>(dsl + tile_off<S::DS_ROWB>(wave * 32 + col, ql * 2), u32x2{sw[2 * k], sw[2 * k + 1]});
+        }
+        pf[2 * qb + u] = Raw{pw[0], pw[1], pw[2], pw[3]};
+        sf[2 * qb + u] = Raw{sw[0], sw[1], sw[2], sw[3]};
+      }
+    }
+
+    // dV^T += dO^T P and dK^T += Q^T dS (A operands read transposed).
+#pragma unroll
+    for (int dt = 0; dt < S::NDT; ++dt) {
+#pragma unroll
+      for (int p = 0; p < S::NP; ++p) {
+        dvt[dt] = E::mma(tr_operand<ROWB, false>(stage + S::OFF_DO, 16 * p, 32 * dt, lane), pf[p], dvt[dt]);
+        dkt[dt] = E::mma(tr_operand<ROWB, false>(stage, 16 * p, 32 * dt, lane), sf[p], dkt[dt]);
+      }
+    }
+    __syncthreads();  // dS of all four waves is in LDS
+
+    // dQ[q, d] += sum over the 128 keys of dS[q, key] K[key, d] (unscaled):
+    // C = dQ block (lane = head-dim column, registers = query rows).
+#pragma unroll
+    for (int n = 0; n < S::DQ_UNITS; ++n) {
+      const int qb = qb0 + n * (4 / S::NDT);
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int t = 0; t < S::NKT; ++t)
+        acc = E::mma(tr_operand<S::DS_ROWB, true>(dsl, 16 * t, 32 * qb, lane), kq[t], acc);
+      float* dst = dQacc + (size_t)(q0 + 32 * qb + 4 * half) * D + dblk * 32 + col;
+      if (q0 + kStepQ <= N) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          unsafeAtomicAdd(dst + (8 * (r >> 2) + (r & 3)) * D, acc[r]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (q0 + 32 * qb + 8 * (r >> 2) + 4 * half + (r & 3) < N)
+            unsafeAtomicAdd(dst + (8 * (r >> 2) + (r & 3)) * D, acc[r]);
+      }
+    }
+
+    if (it + 1 < nq) store(lds + ((it + 1 - it0) & 1) * S::STAGE);
+    __syncthreads();
+  }
+
+  // Epilogue: lane = key, registers = head-dim rows of dK^T / dV^T.
+  if (key >= N) return;
+  T* dkrow = dK + (size_t)key * D;
+  T* dvrow = dV + (size_t)key * D;
+  const float sc = a.scale;
+#pragma unroll
+  for (int dt = 0; dt < S::NDT; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = dt * 32 + 8 * g + 4 * half;
+      const f32x16& kk = dkt[dt];
+      const f32x16& vv = dvt[dt];
+      st<u32x2>(dkrow + d0,
+                u32x2{E::bits(kk[4 * g] * sc) | ((uint32_t)E::bits(kk[4 * g + 1] * sc) << 16),
+                      E::bits(kk[4 * g + 2] * sc) | ((uint32_t)E::bits(kk[4 * g + 3] * sc) << 16)});
+      st<u32x2>(dvrow + d0, u32x2{E::bits(vv[4 * g]) | ((uint32_t)E::bits(vv[4 * g + 1]) << 16),
+                                  E::bits(vv[4 * g + 2]) | ((uint32_t)E::bits(vv[4 * g + 3]) << 16)});
+    }
+}
+
 // D_i = sum_k dO_ik O_ik (float32) and dQ accumulator rows cleared.
 // TPR threads per row, 16 bytes of O and dO each.
 template <typename T, int D>
@@ -434,8 +747,13 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
     void* kargs[] = {&args};
     const int nkt = (a.N + kBN - 1) / kBN;
     const dim3 grid((unsigned)((long long)a.B * a.H * nkt));
-    const void* fn = a.causal ? reinterpret_cast<const void*>(&bwd_main_kernel<T, D, true>)
-                              : reinterpret_cast<const void*>(&bwd_main_kernel<T, D, false>);
+    const void* fn;
+    if constexpr (sizeof(T) == 2)
+      fn = a.causal ? reinterpret_cast<const void*>(&bwd16_kernel<T, D, true>)
+                    : reinterpret_cast<const void*>(&bwd16_kernel<T, D, false>);
+    else
+      fn = a.causal ? reinterpret_cast<const void*>(&bwd_main_kernel<T, D, true>)
+                    : reinterpret_cast<const void*>(&bwd_main_kernel<T, D, false>);
     hipError_t e = hipLaunchKernel(fn, grid, dim3(kThreads), kargs, 0, stream);
     if (e != hipSuccess) return e;
   }
