@@ -572,14 +572,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd16_kernel(BwdArgs a) {
     if (tid < 2 * kStepQ) st<float>(stage + S::OFF_LSE + tid * 4, stat);
   };
 
-  load(it0 * kStepQ);
+  // The steps [it0, nq) are visited starting at a per-workgroup offset, so
+  // that the workgroups of a head (which run concurrently on one XCD) add
+  // into different dQ rows at any moment instead of all contending for the
+  // same cache lines.
+  const int ns = nq - it0;
+  const int shift = (int)((long long)(k0 / kBN) * ns / nkt);
+  auto step_q0 = [&](int j) {
+    const int t = j + shift;
+    return (it0 + (t >= ns ? t - ns : t)) * kStepQ;
+  };
+  load(step_q0(0));
   store(lds);
   __syncthreads();
 
-  for (int it = it0; it < nq; ++it) {
-    const char* stage = lds + ((it - it0) & 1) * S::STAGE;
-    const int q0 = it * kStepQ;
-    if (it + 1 < nq) load(q0 + kStepQ);
+  for (int j = 0; j < ns; ++j) {
+    const char* stage = lds + (j & 1) * S::STAGE;
+    const int q0 = step_q0(j);
+    if (j + 1 < ns) load(step_q0(j + 1));
 
     // Per 32-query block: S = Q K^T and dP = dO V^T (lane = key, registers
     // = queries); P = exp2(S*scale*log2e - LSE*log2e) and dS = P * (dP - D),
@@ -663,7 +673,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd16_kernel(BwdArgs a) {
       }
     }
 
-    if (it + 1 < nq) store(lds + ((it + 1 - it0) & 1) * S::STAGE);
+    if (j + 1 < ns) store(lds + ((j + 1) & 1) * S::STAGE);
     __syncthreads();
   }
 
