@@ -105,12 +105,22 @@ def cpu_baseline(w, inputs, budget_s=10.0, max_s=30.0):
                       f"{len(os.sched_getaffinity(0))} cores, BLAS threads {threads}"}
 
 
-def time_calls(fn, steps, warmup, events_per_call):
-    """Run fn() warmup+steps times; returns (total_ms, [per-call event ms lists])."""
+def time_calls(fn, steps, warmup, events_per_call, warmup_s=0.0):
+    """Run fn() warmup+steps times; returns (total_ms, [per-call event ms lists]).
+
+    The untimed warm-up runs at least `warmup` steps and at least `warmup_s`
+    seconds: the GPU's clock ramps up over the first second of sustained
+    load, and a short warm-up would time the ramp instead of the kernels.
+    """
     import torch
 
-    for _ in range(warmup):
+    t0 = time.perf_counter()
+    done = 0
+    while done < warmup or time.perf_counter() - t0 < warmup_s:
         fn(None)
+        done += 1
+        if done % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(events_per_call + 1)]
           for _ in range(steps)]
@@ -164,7 +174,7 @@ def run_main(args):
                 ev[j].record()
 
     n_ev = int(do_fwd) + int(do_bwd)
-    total_ms, per = time_calls(step, args.steps, args.warmup, n_ev)
+    total_ms, per = time_calls(step, args.steps, args.warmup, n_ev, args.warmup_seconds)
     ms_step = total_ms / args.steps
     fwd_flop, bwd_flop = w.fwd_flops(), w.bwd_flops()
     flop = fwd_flop * do_fwd + bwd_flop * do_bwd
@@ -181,8 +191,8 @@ def run_main(args):
     }
     j, roofs = 0, {}
     for name, on, fl, kern in (
-            ("fwd", do_fwd, fwd_flop, "fwd_kernel (the one kernel of fa_fwd)"),
-            ("bwd", do_bwd, bwd_flop, "fa_bwd: bwd_main_kernel (all MFMA work) + bwd_pre_kernel"
+            ("fwd", do_fwd, fwd_flop, "fwd_pp_kernel (the one kernel of fa_fwd)"),
+            ("bwd", do_bwd, bwd_flop, "fa_bwd: bwd16_kernel (all MFMA work) + bwd_pre_kernel"
                                       " + bwd_dq_kernel (memory-bound, <1% of the call)")):
         if not on:
             continue
@@ -233,7 +243,8 @@ def run_copy(args):
 
 def _short(name: str) -> str:
     """Readable kernel name from a (possibly mangled) symbol."""
-    m = re.search(r"(fwd_kernel|bwd_main_kernel|bwd_pre_kernel|bwd_dq_kernel)I([^E]*)", name)
+    m = re.search(r"(fwd_pp_kernel|fwd_kernel|bwd16_kernel|bwd_main_kernel|bwd_pre_kernel|bwd_dq_kernel)"
+                  r"I([^E]*)", name)
     if m:
         return m.group(1) + "<" + m.group(2).replace("DF16b", "bf16,").replace("DF16_", "f16,")\
             .replace("Li", "d=").replace("Lb0", ",noncausal").replace("Lb1", ",causal") + ">"
@@ -269,8 +280,10 @@ def summarize(path):
 def main():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--warmup-seconds", type=float, default=1.5,
+                   help="minimum untimed warm-up time (clock ramp-up), in seconds")
     p.add_argument("--workload", default="bf16_n16k_d128")
     p.add_argument("--only", choices=["fwd", "bwd"])
     p.add_argument("--no-cpu-baseline", action="store_true")
