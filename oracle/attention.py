@@ -33,6 +33,16 @@ Readings taken where the pages are silent (each also listed in the design doc):
     the definition (chain rule through softmax), written out below.
   * in the blockwise recurrence, a row that sees no key inside one block
     contributes nothing from that block (its block max is -inf, its block sum 0).
+  * local window (the block-sparse / sliding-window variant the survey
+    ranks next; the pages only show the causal special case): key j is
+    visible to query i when i - left <= j <= i + right, a negative bound
+    meaning unbounded on that side; combined with the causal rule when both
+    are given. Causal is the window (unbounded, 0).
+  * grouped K/V heads (multi-query / grouped-query attention, named next to
+    the method on the pages' overview of later work): with Hq query heads
+    and Hkv K/V heads (Hkv divides Hq), query head h attends with K/V head
+    h // (Hq / Hkv). The gradient of a K/V head is the sum over the query
+    heads that use it.
 """
 
 from __future__ import annotations
@@ -56,14 +66,44 @@ def _f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def _visible(q_pos: np.ndarray, n_keys: int, causal: bool) -> np.ndarray | None:
+def _visible(q_pos: np.ndarray, n_keys: int, causal: bool, window=None) -> np.ndarray | None:
     """Boolean [rows, n_keys] mask of keys each query may attend to (None = all).
 
     Causal reading: query at absolute position i sees keys 0..i.
+    Window (left, right): query i sees keys i-left .. i+right (negative = unbounded).
     """
-    if not causal:
-        return None
-    return np.arange(n_keys)[None, :] <= q_pos[:, None]
+    vis = None
+    if causal:
+        vis = np.arange(n_keys)[None, :] <= q_pos[:, None]
+    if window is not None:
+        left, right = window
+        keys = np.arange(n_keys)[None, :]
+        if left >= 0:
+            lo = keys >= q_pos[:, None] - left
+            vis = lo if vis is None else vis & lo
+        if right >= 0:
+            hi = keys <= q_pos[:, None] + right
+            vis = hi if vis is None else vis & hi
+    return vis
+
+
+def _expand_kv(q, k, v):
+    """K/V heads repeated so that query head h uses K/V head h // (Hq / Hkv)."""
+    if k.ndim < 3 or k.shape[-3] == q.shape[-3]:
+        return k, v
+    hq, hkv = q.shape[-3], k.shape[-3]
+    if hkv < 1 or hq % hkv:
+        raise ValueError("the number of K/V heads must divide the number of query heads")
+    group = hq // hkv
+    return np.repeat(k, group, axis=-3), np.repeat(v, group, axis=-3)
+
+
+def _reduce_kv_grad(g, hkv):
+    """Sum a per-query-head K/V gradient over the query heads of each group."""
+    if g.shape[-3] == hkv:
+        return g
+    group = g.shape[-3] // hkv
+    return g.reshape(g.shape[:-3] + (hkv, group) + g.shape[-2:]).sum(axis=-3)
 
 
 def _scores(qc: np.ndarray, k: np.ndarray, scale: float, vis) -> np.ndarray:
@@ -78,7 +118,7 @@ def _scores(qc: np.ndarray, k: np.ndarray, scale: float, vis) -> np.ndarray:
     return s
 
 
-def _head_forward(q, k, v, scale, causal, q_pos):
+def _head_forward(q, k, v, scale, causal, q_pos, window=None):
     """Three-pass safe softmax attention for one head.
 
     Pass 1: row max m of the scaled scores.     [FA-mem §2.2 safe softmax]
@@ -92,7 +132,7 @@ def _head_forward(q, k, v, scale, causal, q_pos):
     lse = np.empty(n_rows, dtype=np.float64)
     for r0 in range(0, n_rows, ROW_CHUNK):
         r1 = min(r0 + ROW_CHUNK, n_rows)
-        vis = _visible(q_pos[r0:r1], k.shape[0], causal)
+        vis = _visible(q_pos[r0:r1], k.shape[0], causal, window)
         s = _scores(q[r0:r1], k, scale, vis)
         m = s.max(axis=1, keepdims=True)                 # pass 1
         e = np.exp(s - m)
@@ -115,38 +155,42 @@ def _batched(fn, arrays, n_out):
     return [np.stack(o).reshape(lead + o[0].shape) for o in outs]
 
 
-def attention_forward(q, k, v, scale: float, causal: bool, q_positions=None):
-    """O = softmax(scale * Q K^T [causal-masked]) V and the per-row LSE.
+def attention_forward(q, k, v, scale: float, causal: bool, q_positions=None, window=None):
+    """O = softmax(scale * Q K^T [masked]) V and the per-row LSE.
 
-    Shapes: q [..., Nq, d], k [..., Nk, d], v [..., Nk, dv] (leading dims are
-    batch and heads). ``q_positions`` gives the absolute position of each query
-    row for the causal mask (default 0..Nq-1), which lets a caller evaluate a
-    sampled subset of rows of a long sequence exactly.
+    Shapes: q [..., Hq, Nq, d], k [..., Hkv, Nk, d], v [..., Hkv, Nk, dv]
+    (leading dims are batch and heads; Hkv divides Hq, see _expand_kv; plain
+    multi-head attention has Hkv = Hq). ``q_positions`` gives the absolute
+    position of each query row for the causal and window masks (default
+    0..Nq-1), which lets a caller evaluate a sampled subset of rows of a long
+    sequence exactly. ``window`` = (left, right) or None.
 
-    Returns (O [..., Nq, dv], LSE [..., Nq]), float64.
+    Returns (O [..., Hq, Nq, dv], LSE [..., Hq, Nq]), float64.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
+    k, v = _expand_kv(q, k, v)
     pos = np.arange(q.shape[-2]) if q_positions is None else np.asarray(q_positions)
     if pos.shape != (q.shape[-2],):
         raise ValueError("q_positions must have one entry per query row")
-    return tuple(_batched(lambda a, b, c: _head_forward(a, b, c, scale, causal, pos),
+    return tuple(_batched(lambda a, b, c: _head_forward(a, b, c, scale, causal, pos, window),
                           [q, k, v], 2))
 
 
-def attention_probabilities(q, k, scale: float, causal: bool):
+def attention_probabilities(q, k, scale: float, causal: bool, window=None):
     """P = softmax(scale * Q K^T) materialized ([..., N, N]; tests only)."""
     q, k = _f64(q), _f64(k)
+    k, _ = _expand_kv(q, k, k)
     pos = np.arange(q.shape[-2])
 
     def one(a, b):
-        s = _scores(a, b, scale, _visible(pos, b.shape[0], causal))
+        s = _scores(a, b, scale, _visible(pos, b.shape[0], causal, window))
         e = np.exp(s - s.max(axis=1, keepdims=True))
         return (e / e.sum(axis=1, keepdims=True),)
 
     return _batched(one, [q, k], 1)[0]
 
 
-def _head_backward(q, k, v, do, scale, causal):
+def _head_backward(q, k, v, do, scale, causal, window=None):
     """Gradients of sum(dO * O) for one head, from the definition.
 
     Not on the pages (the answer's step 6 only says the scores are recomputed
@@ -166,7 +210,7 @@ def _head_backward(q, k, v, do, scale, causal):
     dsum = np.empty(n)
     for r0 in range(0, n, ROW_CHUNK):
         r1 = min(r0 + ROW_CHUNK, n)
-        s = _scores(q[r0:r1], k, scale, _visible(pos[r0:r1], k.shape[0], causal))
+        s = _scores(q[r0:r1], k, scale, _visible(pos[r0:r1], k.shape[0], causal, window))
         e = np.exp(s - s.max(axis=1, keepdims=True))
         p = e / e.sum(axis=1, keepdims=True)
         dv += p.T @ do[r0:r1]
@@ -179,15 +223,21 @@ def _head_backward(q, k, v, do, scale, causal):
     return dq, dk, dv, dsum
 
 
-def attention_backward(q, k, v, do, scale: float, causal: bool):
+def attention_backward(q, k, v, do, scale: float, causal: bool, window=None):
     """(dQ, dK, dV, D) for the loss sum(dO * O), all float64.
 
     D is the per-row term sum_j P_ij dP_ij (returned so tests can check that it
-    equals rowsum(dO * O)).
+    equals rowsum(dO * O)). With grouped K/V heads, dK and dV have the K/V
+    head count: each is the sum over the query heads that use that K/V head.
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
-    return tuple(_batched(lambda a, b, c, g: _head_backward(a, b, c, g, scale, causal),
-                          [q, k, v, do], 4))
+    hkv = k.shape[-3] if k.ndim >= 3 else None
+    k, v = _expand_kv(q, k, v)
+    dq, dk, dv, dsum = _batched(
+        lambda a, b, c, g: _head_backward(a, b, c, g, scale, causal, window), [q, k, v, do], 4)
+    if hkv is not None:
+        dk, dv = _reduce_kv_grad(dk, hkv), _reduce_kv_grad(dv, hkv)
+    return dq, dk, dv, dsum
 
 
 def _head_blockwise(q, k, v, scale, causal, block_q, block_k):

@@ -291,3 +291,132 @@ def test_matches_torch_cpu_float64_attention_and_autograd(causal):
     np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-11)
     np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-11)
     np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-11)
+
+
+# --------------------------------------------------------------- windows and grouped K/V heads
+WINDOWS = [(0, 0), (1, 0), (0, 2), (2, 1), (3, -1), (-1, 2)]
+
+
+def brute_force_general(q, k, v, scale, causal, window):
+    """Pure-Python loops over heads, rows and keys with the visibility rule
+    spelled out; query head h uses K/V head h // (Hq / Hkv)."""
+    hq, hkv = len(q), len(k)
+    group = hq // hkv
+    o, lse = [], []
+    for h in range(hq):
+        kh, vh = k[h // group], v[h // group]
+        oh, lh = [], []
+        for i in range(len(q[h])):
+            w = []
+            for j in range(len(kh)):
+                vis = not (causal and j > i)
+                if window[0] >= 0 and j < i - window[0]:
+                    vis = False
+                if window[1] >= 0 and j > i + window[1]:
+                    vis = False
+                w.append(math.exp(scale * sum(a * b for a, b in zip(q[h][i], kh[j]))) if vis else 0.0)
+            z = sum(w)
+            lh.append(math.log(z))
+            oh.append([sum(w[j] * vh[j][c] for j in range(len(kh))) / z for c in range(len(vh[0]))])
+        o.append(oh)
+        lse.append(lh)
+    return np.array(o), np.array(lse)
+
+
+@pytest.mark.parametrize("window", WINDOWS)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("hq,hkv", [(1, 1), (2, 1), (4, 2)])
+def test_brute_force_window_and_groups(window, causal, hq, hkv):
+    n, d = 7, 3
+    seed = 7 * hq + 3 * hkv + 11 * causal + window[0] * 5 + window[1]
+    q, k, v = rand((hq, n, d), seed), rand((hkv, n, d), seed + 1), rand((hkv, n, d + 1), seed + 2)
+    o, lse = attention_forward(q, k, v, 0.61, causal, window=window)
+    bo, blse = brute_force_general(q.tolist(), k.tolist(), v.tolist(), 0.61, causal, window)
+    np.testing.assert_allclose(o, bo, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, blse, rtol=0, atol=1e-12)
+
+
+def test_window_closed_forms():
+    q, k, v = rand((2, 20, 5), 81), rand((2, 20, 5), 82), rand((2, 20, 3), 83)
+    # Each row sees only its own key: O = V, LSE = scale * q_i . k_i.
+    o, lse = attention_forward(q, k, v, 0.4, False, window=(0, 0))
+    np.testing.assert_allclose(o, v, atol=1e-14)
+    np.testing.assert_allclose(lse, 0.4 * (q * k).sum(-1), atol=1e-14)
+    # A window covering every key is plain attention; (unbounded, 0) is causal.
+    full = attention_forward(q, k, v, 0.4, False)
+    for a, b in zip(attention_forward(q, k, v, 0.4, False, window=(19, 25)), full):
+        np.testing.assert_allclose(a, b, atol=1e-14)
+    causal = attention_forward(q, k, v, 0.4, True)
+    for a, b in zip(attention_forward(q, k, v, 0.4, False, window=(-1, 0)), causal):
+        np.testing.assert_allclose(a, b, atol=1e-14)
+
+
+def test_grouped_heads_equal_repeated_heads_and_mqa_closed_form():
+    q, k, v = rand((2, 6, 9, 4), 91), rand((2, 3, 9, 4), 92), rand((2, 3, 9, 4), 93)
+    o, lse = attention_forward(q, k, v, 0.5, True)
+    # Query heads 2g and 2g+1 share K/V head g.
+    for h in range(6):
+        oh, lh = attention_forward(q[:, h], k[:, h // 2], v[:, h // 2], 0.5, True)
+        np.testing.assert_allclose(o[:, h], oh, atol=1e-14)
+        np.testing.assert_allclose(lse[:, h], lh, atol=1e-14)
+    # One K/V head and identical query heads: identical outputs, and the K/V
+    # gradients are the per-head gradients times the number of heads.
+    q1 = np.repeat(rand((1, 1, 9, 4), 94), 4, axis=1)
+    k1, v1, do1 = rand((1, 1, 9, 4), 95), rand((1, 1, 9, 4), 96), np.repeat(rand((1, 1, 9, 4), 97), 4, axis=1)
+    o1, _ = attention_forward(q1, k1, v1, 0.5, False)
+    np.testing.assert_allclose(o1, np.repeat(o1[:, :1], 4, axis=1), atol=1e-14)
+    _, dk1, dv1, _ = attention_backward(q1, k1, v1, do1, 0.5, False)
+    _, dk0, dv0, _ = attention_backward(q1[:, :1], k1, v1, do1[:, :1], 0.5, False)
+    np.testing.assert_allclose(dk1, 4 * dk0, atol=1e-12)
+    np.testing.assert_allclose(dv1, 4 * dv0, atol=1e-12)
+
+
+@pytest.mark.parametrize("window", [(2, 1), (4, -1), (-1, 3)])
+def test_window_gradients_match_finite_differences(window):
+    n, d = 6, 3
+    q, k, v, do = (rand((n, d), 150 + i) for i in range(4))
+    scale = 0.7
+    dq, dk, dv, _ = attention_backward(q, k, v, do, scale, False, window=window)
+
+    def loss(qq, kk, vv):
+        return float((attention_forward(qq, kk, vv, scale, False, window=window)[0] * do).sum())
+
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = dict(args_p)
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p[name], args_m[name] = xp, xm
+            fd[idx] = (loss(args_p["q"], args_p["k"], args_p["v"])
+                       - loss(args_m["q"], args_m["k"], args_m["v"])) / (2 * h)
+        np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+@pytest.mark.parametrize("window,causal", [((5, 3), False), ((7, -1), True), ((-1, -1), True), ((0, 9), False)])
+def test_grouped_window_matches_torch_float64_and_autograd(window, causal):
+    b, hq, hkv, n, d = 2, 4, 2, 33, 8
+    q, do = rand((b, hq, n, d), 170), rand((b, hq, n, d), 171)
+    k, v = rand((b, hkv, n, d), 172), rand((b, hkv, n, d), 173)
+    scale = 0.3
+    i, j = np.arange(n)[:, None], np.arange(n)[None, :]
+    vis = np.ones((n, n), dtype=bool)
+    if causal:
+        vis &= j <= i
+    if window[0] >= 0:
+        vis &= j >= i - window[0]
+    if window[1] >= 0:
+        vis &= j <= i + window[1]
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    to = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, attn_mask=torch.tensor(vis), scale=scale, enable_gqa=True)
+    to.backward(torch.tensor(do))
+    o, _ = attention_forward(q, k, v, scale, causal, window=window)
+    np.testing.assert_allclose(o, to.detach().numpy(), atol=1e-12)
+    dq, dk, dv, _ = attention_backward(q, k, v, do, scale, causal, window=window)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-11)

@@ -19,8 +19,21 @@ SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
 
 MUTATIONS = [
     ("scale dropped from scores", "s = scale * (qc @ k.T)", "s = (qc @ k.T)"),
-    ("causal direction flipped", "<= q_pos[:, None]", ">= q_pos[:, None]"),
-    ("causal hides the diagonal", "<= q_pos[:, None]", "< q_pos[:, None]"),
+    ("causal direction flipped", "np.arange(n_keys)[None, :] <= q_pos[:, None]",
+     "np.arange(n_keys)[None, :] >= q_pos[:, None]"),
+    ("causal hides the diagonal", "np.arange(n_keys)[None, :] <= q_pos[:, None]",
+     "np.arange(n_keys)[None, :] < q_pos[:, None]"),
+    ("window left bound off by one", "lo = keys >= q_pos[:, None] - left",
+     "lo = keys > q_pos[:, None] - left"),
+    ("window right bound off by one", "hi = keys <= q_pos[:, None] + right",
+     "hi = keys < q_pos[:, None] + right"),
+    ("window sides swapped", "lo = keys >= q_pos[:, None] - left",
+     "lo = keys >= q_pos[:, None] - right"),
+    ("grouped heads interleaved instead of blocked",
+     "return np.repeat(k, group, axis=-3), np.repeat(v, group, axis=-3)",
+     "return np.tile(k, (group, 1, 1)), np.tile(v, (group, 1, 1))"),
+    ("grouped K/V gradient averaged instead of summed",
+     "+ g.shape[-2:]).sum(axis=-3)", "+ g.shape[-2:]).mean(axis=-3)"),
     ("max over the wrong axis", "m = s.max(axis=1, keepdims=True)",
      "m = s.max(axis=0, keepdims=True)"),
     ("LSE without the max", "lse[r0:r1] = (m + np.log(l))[:, 0]",
@@ -68,6 +81,12 @@ PINS = [
     (T.test_gradients_match_finite_differences, dict(causal=False)),
     (T.test_gradient_invariants, dict(causal=True)),
     (T.test_matches_torch_cpu_float64_attention_and_autograd, dict(causal=True)),
+    (T.test_brute_force_window_and_groups, dict(window=(2, 1), causal=False, hq=4, hkv=2)),
+    (T.test_brute_force_window_and_groups, dict(window=(1, 0), causal=True, hq=2, hkv=1)),
+    (T.test_window_closed_forms, {}),
+    (T.test_grouped_heads_equal_repeated_heads_and_mqa_closed_form, {}),
+    (T.test_window_gradients_match_finite_differences, dict(window=(2, 1))),
+    (T.test_grouped_window_matches_torch_float64_and_autograd, dict(window=(5, 3), causal=False)),
 ]
 
 
