@@ -1,24 +1,29 @@
 """MI355X (gfx950) IO-aware exact attention: Python binding of libfa.so.
 
-The functions named like the C ABI (``fa_fwd``, ``fa_bwd``,
-``fa_bwd_workspace_size``, ``fa_strerror``) only marshal arguments: they
-read shapes, dtype, device pointers and the current HIP stream from torch
-tensors and call the library, which does every step of the computation in
-its own kernels. ``forward``/``backward`` additionally allocate the outputs
-(and the backward workspace) with torch. There is no fallback: if libfa.so
-is missing, or a tensor is not on the GPU, these raise.
+The functions named like the C ABI (``fa_fwd``, ``fa_bwd``, ``fa_fwd_ex``,
+``fa_bwd_ex``, ``fa_bwd_workspace_size``, ``fa_strerror``) only marshal
+arguments: they read shapes, dtype, device pointers and the current HIP
+stream from torch tensors and call the library, which does every step of the
+computation in its own kernels. ``forward``/``backward`` additionally
+allocate the outputs (and the backward workspace) with torch. There is no
+fallback: if libfa.so is missing, or a tensor is not on the GPU, these raise.
+
+Grouped K/V heads are expressed by the shape of k and v ([B, Hkv, N, d] with
+Hkv dividing H); a local window by ``window=(left, right)`` where a negative
+(or None) bound is unbounded on that side.
 """
 
 from __future__ import annotations
 
+import ctypes
 import math
 
 import torch
 
 from . import _lib
 
-__all__ = ["FaError", "fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_strerror",
-           "forward", "backward", "DTYPES"]
+__all__ = ["FaError", "fa_fwd", "fa_bwd", "fa_fwd_ex", "fa_bwd_ex", "fa_bwd_workspace_size",
+           "fa_strerror", "forward", "backward", "DTYPES"]
 
 DTYPES = {torch.float32: _lib.FA_F32, torch.float16: _lib.FA_F16,
           torch.bfloat16: _lib.FA_BF16}
@@ -93,26 +98,95 @@ def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool, workspac
         raise FaError(st, "fa_bwd")
 
 
+def _kv_shape(q, k):
+    B, H, N, d = _shape(q)
+    if k.dim() != 4:
+        raise ValueError("k must be [B, Hkv, N, d]")
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, N, d) or Hkv < 1 or H % Hkv:
+        raise ValueError(f"k: expected [B, Hkv, N, d] with Hkv dividing H={H}, got "
+                         f"{tuple(k.shape)}")
+    return B, H, Hkv, N, d
+
+
+def _options(Hkv: int, window):
+    wl, wr = (None, None) if window is None else window
+    wl = -1 if wl is None or wl < 0 else int(wl)
+    wr = -1 if wr is None or wr < 0 else int(wr)
+    return _lib.FaOptions(Hkv, wl, wr)
+
+
+def fa_fwd_ex(q, k, v, o, lse, scale: float, causal: bool, window=None, stream=None) -> None:
+    """fa_fwd with grouped K/V heads (from k's shape) and a local window."""
+    B, H, Hkv, N, d = _kv_shape(q, k)
+    _check({"q": q, "o": o}, (B, H, N, d), q.dtype)
+    _check({"k": k, "v": v}, (B, Hkv, N, d), q.dtype)
+    _check({"lse": lse}, (B, H, N), torch.float32)
+    opts = _options(Hkv, window)
+    with torch.cuda.device(q.device):
+        st = _lib.load().fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                   lse.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
+                                   DTYPES[q.dtype], ctypes.byref(opts), _stream(q, stream))
+    if st != _lib.FA_OK:
+        raise FaError(st, "fa_fwd_ex")
+
+
+def fa_bwd_ex(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool, workspace,
+              window=None, stream=None) -> None:
+    """fa_bwd with grouped K/V heads (from k's shape) and a local window."""
+    B, H, Hkv, N, d = _kv_shape(q, k)
+    _check({"q": q, "o": o, "do": do, "dq": dq}, (B, H, N, d), q.dtype)
+    _check({"k": k, "v": v, "dk": dk, "dv": dv}, (B, Hkv, N, d), q.dtype)
+    _check({"lse": lse}, (B, H, N), torch.float32)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    opts = _options(Hkv, window)
+    with torch.cuda.device(q.device):
+        st = _lib.load().fa_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                   do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                   dv.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
+                                   DTYPES[q.dtype], ctypes.byref(opts), workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(),
+                                   _stream(q, stream))
+    if st != _lib.FA_OK:
+        raise FaError(st, "fa_bwd_ex")
+
+
+def _plain(q, k, window) -> bool:
+    return window is None and k.dim() == 4 and k.shape[1] == q.shape[1]
+
+
 def _default_scale(d: int, scale):
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
 
-def forward(q, k, v, causal: bool = False, scale: float | None = None, stream=None):
-    """Allocate O and LSE with torch and run fa_fwd; returns (o, lse)."""
+def forward(q, k, v, causal: bool = False, scale: float | None = None, stream=None,
+            window=None):
+    """Allocate O and LSE with torch and run fa_fwd (fa_fwd_ex when k, v have
+    fewer heads than q or a window is given); returns (o, lse)."""
     B, H, N, d = _shape(q)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    fa_fwd(q, k, v, o, lse, _default_scale(d, scale), causal, stream)
+    if _plain(q, k, window):
+        fa_fwd(q, k, v, o, lse, _default_scale(d, scale), causal, stream)
+    else:
+        fa_fwd_ex(q, k, v, o, lse, _default_scale(d, scale), causal, window, stream)
     return o, lse
 
 
 def backward(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None,
-             stream=None, workspace=None):
-    """Allocate dQ, dK, dV (and the workspace unless given) and run fa_bwd."""
+             stream=None, workspace=None, window=None):
+    """Allocate dQ, dK, dV (and the workspace unless given) and run fa_bwd
+    (fa_bwd_ex when k, v have fewer heads than q or a window is given)."""
     B, H, N, d = _shape(q)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if workspace is None:
         workspace = torch.empty(fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8,
                                 device=q.device)
-    fa_bwd(q, k, v, o, do, lse, dq, dk, dv, _default_scale(d, scale), causal, workspace, stream)
+    if _plain(q, k, window):
+        fa_bwd(q, k, v, o, do, lse, dq, dk, dv, _default_scale(d, scale), causal, workspace,
+               stream)
+    else:
+        fa_bwd_ex(q, k, v, o, do, lse, dq, dk, dv, _default_scale(d, scale), causal, workspace,
+                  window, stream)
     return dq, dk, dv

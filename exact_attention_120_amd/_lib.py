@@ -16,12 +16,24 @@ FA_OK = 0
 _c = ctypes
 _vp, _int, _flt, _sz = _c.c_void_p, _c.c_int, _c.c_float, _c.c_size_t
 
+
+class FaOptions(_c.Structure):
+    """struct fa_options of include/fa.h."""
+    _fields_ = [("kv_heads", _int), ("window_left", _int), ("window_right", _int)]
+
+
+_opt = _c.POINTER(FaOptions)
+
 # name -> (restype, argtypes); must match include/fa.h.
 SIGNATURES = {
     "fa_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _flt, _int, _int, _vp]),
     "fa_bwd_workspace_size": (_sz, [_int, _int, _int, _int]),
     "fa_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int,
                       _flt, _int, _int, _vp, _sz, _vp]),
+    "fa_fwd_ex": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _flt, _int, _int,
+                         _opt, _vp]),
+    "fa_bwd_ex": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int,
+                         _flt, _int, _int, _opt, _vp, _sz, _vp]),
     "fa_strerror": (_c.c_char_p, [_int]),
 }
 

@@ -52,26 +52,52 @@ int check_shape(int B, int H, int N, int d, float scale, int causal, int dtype) 
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
+// Options with defaults filled in; FA_OK or FA_ERR_INVALID_ARG.
+struct Opts {
+  int Hkv, wl, wr;
+};
+int read_opts(const fa_options* o, int H, Opts* out) {
+  out->Hkv = H;
+  out->wl = out->wr = -1;
+  if (!o) return FA_OK;
+  if (o->kv_heads < 0 || (o->kv_heads > 0 && H % o->kv_heads != 0)) return FA_ERR_INVALID_ARG;
+  out->Hkv = o->kv_heads == 0 ? H : o->kv_heads;
+  out->wl = o->window_left < 0 ? -1 : o->window_left;
+  out->wr = o->window_right < 0 ? -1 : o->window_right;
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-           int N, int d, float scale, int causal, int dtype, void* stream) {
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+              int N, int d, float scale, int causal, int dtype, const fa_options* opts,
+              void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   int st = check_shape(B, H, N, d, scale, causal, dtype);
   if (st != FA_OK) return st;
+  Opts op;
+  if ((st = read_opts(opts, H, &op)) != FA_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_ALIGN;
   const size_t tb = (size_t)B * H * N * d * elem_size(dtype);
+  const size_t kb = (size_t)B * op.Hkv * N * d * elem_size(dtype);
   const size_t lb = (size_t)B * H * N * sizeof(float);
-  const void* ins[] = {q, k, v};
-  for (const void* in : ins)
-    if (overlap(o, tb, in, tb) || overlap(lse, lb, in, tb)) return FA_ERR_INVALID_ARG;
+  struct Range { const void* p; size_t n; };
+  const Range ins[] = {{q, tb}, {k, kb}, {v, kb}};
+  for (const Range& in : ins)
+    if (overlap(o, tb, in.p, in.n) || overlap(lse, lb, in.p, in.n)) return FA_ERR_INVALID_ARG;
   if (overlap(o, tb, lse, lb)) return FA_ERR_INVALID_ARG;
 
-  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, exp2_scale(scale), causal, dtype};
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, exp2_scale(scale), causal, dtype,
+                op.Hkv, op.wl, op.wr};
   return hip_status(fa::launch_fwd(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+           int N, int d, float scale, int causal, int dtype, void* stream) {
+  return fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, nullptr, stream);
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
@@ -80,14 +106,16 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
   return round_up(rows * sizeof(float)) + round_up(rows * d * sizeof(float));
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
-           const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
-           float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
-           void* stream) {
+int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dO,
+              const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+              float scale, int causal, int dtype, const fa_options* opts, void* workspace,
+              size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv || !workspace)
     return FA_ERR_INVALID_ARG;
   int st = check_shape(B, H, N, d, scale, causal, dtype);
   if (st != FA_OK) return st;
+  Opts op;
+  if ((st = read_opts(opts, H, &op)) != FA_OK) return st;
   const void* ptrs[] = {q, k, v, o, dO, lse, dq, dk, dv};
   for (const void* p : ptrs)
     if (!aligned16(p)) return FA_ERR_ALIGN;
@@ -96,10 +124,11 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   if (workspace_bytes < need) return FA_ERR_WORKSPACE;
 
   const size_t tb = (size_t)B * H * N * d * elem_size(dtype);
+  const size_t kb = (size_t)B * op.Hkv * N * d * elem_size(dtype);
   const size_t lb = (size_t)B * H * N * sizeof(float);
   struct Range { const void* p; size_t n; };
-  const Range ins[] = {{q, tb}, {k, tb}, {v, tb}, {o, tb}, {dO, tb}, {lse, lb}};
-  const Range outs[] = {{dq, tb}, {dk, tb}, {dv, tb}, {workspace, need}};
+  const Range ins[] = {{q, tb}, {k, kb}, {v, kb}, {o, tb}, {dO, tb}, {lse, lb}};
+  const Range outs[] = {{dq, tb}, {dk, kb}, {dv, kb}, {workspace, need}};
   for (const Range& w : outs) {
     for (const Range& r : ins)
       if (overlap(w.p, w.n, r.p, r.n)) return FA_ERR_INVALID_ARG;
@@ -111,8 +140,16 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   float* dsum = reinterpret_cast<float*>(ws);
   float* dq_acc = reinterpret_cast<float*>(ws + round_up(lb));
   fa::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, dsum, dq_acc,
-                B, H, N, d, scale, exp2_scale(scale), causal, dtype};
+                B, H, N, d, scale, exp2_scale(scale), causal, dtype, op.Hkv, op.wl, op.wr};
   return hip_status(fa::launch_bwd(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+           const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+           float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
+           void* stream) {
+  return fa_bwd_ex(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, nullptr,
+                   workspace, workspace_bytes, stream);
 }
 
 const char* fa_strerror(int status) {

@@ -168,20 +168,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   const int N = a.N;
   const int nkt = (N + kBN - 1) / kBN;
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = lin / nkt;
-  const int ktile = lin % nkt;  // causal: low tiles have the most work, run first
-  const int k0 = ktile * kBN;
+  const int bkv = lin / nkt;  // batch * Hkv + K/V head
+  const int k0 = (lin % nkt) * kBN;
+  const int grp = a.H / a.Hkv;  // query heads sharing this K/V head
+  const int bq0 = (bkv / a.Hkv) * a.H + (bkv % a.Hkv) * grp;  // the first of them
 
-  const size_t head = (size_t)bh * N * D;
-  const T* Q = reinterpret_cast<const T*>(a.q) + head;
-  const T* K = reinterpret_cast<const T*>(a.k) + head;
-  const T* V = reinterpret_cast<const T*>(a.v) + head;
-  const T* dO = reinterpret_cast<const T*>(a.dout) + head;
-  T* dK = reinterpret_cast<T*>(a.dk) + head;
-  T* dV = reinterpret_cast<T*>(a.dv) + head;
-  float* dQacc = a.dq_acc + head;
-  const float* lse = a.lse + (size_t)bh * N;
-  const float* dsum = a.dsum + (size_t)bh * N;
+  const size_t kvhead = (size_t)bkv * N * D;
+  const T* K = reinterpret_cast<const T*>(a.k) + kvhead;
+  const T* V = reinterpret_cast<const T*>(a.v) + kvhead;
+  T* dK = reinterpret_cast<T*>(a.dk) + kvhead;
+  T* dV = reinterpret_cast<T*>(a.dv) + kvhead;
+  // Query-head arrays of query head g of the group.
+  auto qhead = [&](int g) { return (size_t)(bq0 + g) * N; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -228,9 +226,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   }
   __syncthreads();
 
-  const int nq = (N + S::BM - 1) / S::BM;
-  const int it0 = CAUSAL ? k0 / S::BM : 0;  // first query tile reaching these keys
+  // Query tiles [it0, it0 + ns) hold every row that sees a key of the tile;
+  // step j covers query head j / ns, tile it0 + j % ns.
+  const int it0 = first_query_seeing(k0, CAUSAL, a.wr) / S::BM;
+  const int ns = last_query_seeing(min(k0 + kBN, N) - 1, N, a.wl) / S::BM - it0 + 1;
+  const int nsteps = grp * ns;
   const float c = a.scale_log2;
+  auto load_step = [&](QTile<T, D>& t, int j) {
+    const int g = j / ns;
+    const size_t qh = qhead(g);
+    t.load(reinterpret_cast<const T*>(a.q) + qh * D, reinterpret_cast<const T*>(a.dout) + qh * D,
+           a.lse + qh, a.dsum + qh, (it0 + j - g * ns) * S::BM, N, tid);
+  };
 
   f32x16 dkt[S::NDT], dvt[S::NDT];
 #pragma unroll
@@ -240,14 +247,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   }
 
   QTile<T, D> qt;
-  qt.load(Q, dO, lse, dsum, it0 * S::BM, N, tid);
+  load_step(qt, 0);
   qt.store(lds, tid);
   __syncthreads();
 
-  for (int it = it0; it < nq; ++it) {
-    const char* stage = lds + ((it - it0) & 1) * S::STAGE;
-    const int q0 = it * S::BM;
-    if (it + 1 < nq) qt.load(Q, dO, lse, dsum, q0 + S::BM, N, tid);
+  for (int j = 0; j < nsteps; ++j) {
+    const char* stage = lds + (j & 1) * S::STAGE;
+    const int g = j / ns;
+    const int q0 = (it0 + j - g * ns) * S::BM;
+    if (j + 1 < nsteps) load_step(qt, j + 1);
 
     // S = Q K^T and dP = dO V^T (lane = key, registers = queries).
     f32x16 s[S::NQB], dp[S::NQB];
@@ -265,7 +273,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
     }
 
     // P = exp(S*scale - LSE), dS = P * (dP - D); masked entries are 0.
-    const bool need_mask = (CAUSAL && q0 < kw0 + 31) || (kw0 + 31 >= N);
+    const bool need_mask =
+        !block_all_visible(q0, q0 + S::BM - 1, kw0, kw0 + 31, N, CAUSAL, a.wl, a.wr);
     Raw pf[S::NPQ], sf[S::NPQ];
 #pragma unroll
     for (int qb = 0; qb < S::NQB; ++qb) {
@@ -280,7 +289,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
           float p = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c, -l2[e]));
           if (need_mask) {
             const int qrow = q0 + ql + e;
-            if (key >= N || (CAUSAL && key > qrow)) p = 0.f;
+            if (!key_visible(key, qrow, N, CAUSAL, a.wl, a.wr)) p = 0.f;
           }
           s[qb][r] = p;
           dp[qb][r] = p * (dp[qb][r] - dd[e]);
@@ -334,7 +343,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       const char* da = dsl + ((qb * 32 + col) * S::DSS + half * KH) * S::ES;
 #pragma unroll
       for (int t = 0; t < S::NKQ; ++t) acc = E::mma(ld<Raw>(da + t * 2 * KH * S::ES), kq[t], acc);
-      float* dst = dQacc + dblk * 32 + col;
+      float* dst = a.dq_acc + qhead(g) * D + dblk * 32 + col;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qrow = q0 + qb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
@@ -342,7 +351,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       }
     }
 
-    if (it + 1 < nq) qt.store(lds + ((it + 1 - it0) & 1) * S::STAGE, tid);
+    if (j + 1 < nsteps) qt.store(lds + ((j + 1) & 1) * S::STAGE, tid);
     __syncthreads();
   }
 
@@ -471,20 +480,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd16_kernel(BwdArgs a) {
   const int N = a.N;
   const int nkt = (N + kBN - 1) / kBN;
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = lin / nkt;
+  const int bkv = lin / nkt;  // batch * Hkv + K/V head
   const int k0 = (lin % nkt) * kBN;
+  const int grp = a.H / a.Hkv;  // query heads sharing this K/V head
+  const int bq0 = (bkv / a.Hkv) * a.H + (bkv % a.Hkv) * grp;  // the first of them
 
-  const size_t head = (size_t)bh * N * D;
+  const size_t kvhead = (size_t)bkv * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const HeadBuf Q(reinterpret_cast<const T*>(a.q) + head, head_bytes);
-  const HeadBuf K(reinterpret_cast<const T*>(a.k) + head, head_bytes);
-  const HeadBuf V(reinterpret_cast<const T*>(a.v) + head, head_bytes);
-  const HeadBuf G(reinterpret_cast<const T*>(a.dout) + head, head_bytes);
-  T* dK = reinterpret_cast<T*>(a.dk) + head;
-  T* dV = reinterpret_cast<T*>(a.dv) + head;
-  float* dQacc = a.dq_acc + head;
-  const float* lse = a.lse + (size_t)bh * N;
-  const float* dsum = a.dsum + (size_t)bh * N;
+  const HeadBuf K(reinterpret_cast<const T*>(a.k) + kvhead, head_bytes);
+  const HeadBuf V(reinterpret_cast<const T*>(a.v) + kvhead, head_bytes);
+  T* dK = reinterpret_cast<T*>(a.dk) + kvhead;
+  T* dV = reinterpret_cast<T*>(a.dv) + kvhead;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -530,8 +536,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd16_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < S::NQK; ++i) aoff[i] = tile_off<ROWB>(col, (half * (D / 2) + 8 * i) * 2);
 
-  const int nq = (N + kStepQ - 1) / kStepQ;
-  const int it0 = CAUSAL ? k0 / kStepQ : 0;  // first step reaching these keys
+  // Query steps [it0, it0 + ns) hold every row that sees a key of the tile.
+  const int it0 = first_query_seeing(k0, CAUSAL, a.wr) / kStepQ;
+  const int ns = last_query_seeing(min(k0 + kBN, N) - 1, N, a.wl) / kStepQ - it0 + 1;
   const float c = a.scale_log2;
 
   f32x16 dkt[S::NDT], dvt[S::NDT];
@@ -544,7 +551,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd16_kernel(BwdArgs a) {
   // Next step's Q and dO units and one LSE or D value, staged in registers.
   u32x4 sq[S::NLD], sg[S::NLD];
   float stat = 0.f;
-  auto load = [&](int q0) {
+  auto load = [&](int g, int q0) {
+    const size_t qh = (size_t)(bq0 + g) * N;  // query head of the step
+    const HeadBuf Q(reinterpret_cast<const T*>(a.q) + qh * D, head_bytes);
+    const HeadBuf G(reinterpret_cast<const T*>(a.dout) + qh * D, head_bytes);
+    const float* lse = a.lse + qh;
+    const float* dsum = a.dsum + qh;
 #pragma unroll
     for (int j = 0; j < S::NLD; ++j) {
       const int idx = tid + kThreads * j, row = idx / S::UNITS, u = idx % S::UNITS;
@@ -572,31 +584,39 @@ __global__ __launch_bounds__(kThreads, 1) void bwd16_kernel(BwdArgs a) {
     if (tid < 2 * kStepQ) st<float>(stage + S::OFF_LSE + tid * 4, stat);
   };
 
-  // The steps [it0, nq) are visited starting at a per-workgroup offset, so
-  // that the workgroups of a head (which run concurrently on one XCD) add
-  // into different dQ rows at any moment instead of all contending for the
-  // same cache lines.
-  const int ns = nq - it0;
+  // Step j covers query head g = j / ns, query step it0 + (j % ns + shift)
+  // mod ns. Each head's steps are visited starting at a per-workgroup
+  // offset, so that the workgroups of a head (which run concurrently on one
+  // XCD) add into different dQ rows at any moment instead of all contending
+  // for the same cache lines.
   const int shift = (int)((long long)(k0 / kBN) * ns / nkt);
-  auto step_q0 = [&](int j) {
-    const int t = j + shift;
-    return (it0 + (t >= ns ? t - ns : t)) * kStepQ;
+  const int nsteps = grp * ns;
+  auto step_at = [&](int j, int& g, int& q0) {
+    g = j / ns;
+    const int t = j - g * ns + shift;
+    q0 = (it0 + (t >= ns ? t - ns : t)) * kStepQ;
   };
-  load(step_q0(0));
+  int g_next, q_next;
+  step_at(0, g_next, q_next);
+  load(g_next, q_next);
   store(lds);
   __syncthreads();
 
-  for (int j = 0; j < ns; ++j) {
+  for (int j = 0; j < nsteps; ++j) {
     const char* stage = lds + (j & 1) * S::STAGE;
-    const int q0 = step_q0(j);
-    if (j + 1 < ns) load(step_q0(j + 1));
+    const int g = g_next, q0 = q_next;
+    if (j + 1 < nsteps) {
+      step_at(j + 1, g_next, q_next);
+      load(g_next, q_next);
+    }
 
     // Per 32-query block: S = Q K^T and dP = dO V^T (lane = key, registers
     // = queries); P = exp2(S*scale*log2e - LSE*log2e) and dS = P * (dP - D),
     // packed as B operands (P^T, dS^T over the step's queries); dS also goes
     // to LDS. Operand p = 2*qb + u covers registers [8u, 8u+8) of block qb,
     // i.e. queries 16p + 4h + 0..3 and 16p + 8 + 4h + 0..3.
-    const bool need_mask = (CAUSAL && q0 < kw0 + 31) || kw0 + 31 >= N;
+    const bool need_mask =
+        !block_all_visible(q0, q0 + kStepQ - 1, kw0, kw0 + 31, N, CAUSAL, a.wl, a.wr);
     Raw pf[S::NP], sf[S::NP];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -610,7 +630,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd16_kernel(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qrow = q0 + 32 * qb + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key >= N || (CAUSAL && key > qrow)) s[r] = -INFINITY;
+          if (!key_visible(key, qrow, N, CAUSAL, a.wl, a.wr)) s[r] = -INFINITY;
         }
       }
 #pragma unroll
@@ -660,7 +680,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd16_kernel(BwdArgs a) {
 #pragma unroll
       for (int t = 0; t < S::NKT; ++t)
         acc = E::mma(tr_operand<S::DS_ROWB, true>(dsl, 16 * t, 32 * qb, lane), kq[t], acc);
-      float* dst = dQacc + (size_t)(q0 + 32 * qb + 4 * half) * D + dblk * 32 + col;
+      float* dst = a.dq_acc + ((size_t)(bq0 + g) * N + q0 + 32 * qb + 4 * half) * D + dblk * 32 + col;
       if (q0 + kStepQ <= N) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
@@ -673,7 +693,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd16_kernel(BwdArgs a) {
       }
     }
 
-    if (j + 1 < ns) store(lds + ((j + 1) & 1) * S::STAGE);
+    if (j + 1 < nsteps) store(lds + ((j + 1) & 1) * S::STAGE);
     __syncthreads();
   }
 
@@ -756,7 +776,7 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
   {
     void* kargs[] = {&args};
     const int nkt = (a.N + kBN - 1) / kBN;
-    const dim3 grid((unsigned)((long long)a.B * a.H * nkt));
+    const dim3 grid((unsigned)((long long)a.B * a.Hkv * nkt));
     const void* fn;
     if constexpr (sizeof(T) == 2)
       fn = a.causal ? reinterpret_cast<const void*>(&bwd16_kernel<T, D, true>)

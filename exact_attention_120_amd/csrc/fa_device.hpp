@@ -200,6 +200,41 @@ struct BoolC {
   static constexpr bool value = B;
 };
 
+// Visibility of keys to queries: the causal rule (key <= query) and a local
+// window (query - wl <= key <= query + wr; a negative bound is unbounded),
+// plus keys past the sequence end.
+__device__ inline bool key_visible(int key, int q, int N, bool causal, int wl, int wr) {
+  return key < N && (!causal || key <= q) && (wr < 0 || key <= q + wr) && (wl < 0 || key >= q - wl);
+}
+
+// First and last key (inclusive, within [0, N)) visible to any of the query
+// rows r0..r1 (r0 <= r1 < N).
+__device__ inline int first_visible_key(int r0, int wl) { return wl >= 0 ? max(0, r0 - wl) : 0; }
+__device__ inline int last_visible_key(int r1, int N, bool causal, int wr) {
+  int hi = N - 1;
+  if (causal) hi = min(hi, r1);
+  if (wr >= 0) hi = min(hi, r1 + wr);
+  return hi;
+}
+
+// Every key k0..k1 visible to every query r0..r1 (no masking needed).
+__device__ inline bool block_all_visible(int r0, int r1, int k0, int k1, int N, bool causal,
+                                         int wl, int wr) {
+  return k1 < N && (!causal || k1 <= r0) && (wr < 0 || k1 <= r0 + wr) && (wl < 0 || k0 >= r1 - wl);
+}
+
+// The query rows that see at least one key of k0..k1 (k0 <= k1 < N) form the
+// range [first_query_seeing(k0), last_query_seeing(k1)]: key j is visible
+// from query i iff i >= j - r (r = 0 if causal, else window_right when
+// bounded) and i <= j + window_left (when bounded).
+__device__ inline int first_query_seeing(int k0, bool causal, int wr) {
+  const int r = causal ? 0 : wr;
+  return r >= 0 ? max(0, k0 - r) : 0;
+}
+__device__ inline int last_query_seeing(int k1, int N, int wl) {
+  return wl >= 0 ? min(N - 1, k1 + wl) : N - 1;
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs (bid % 8). Remap so
 // that consecutive logical tiles (the query tiles of one head, which read the
 // same K/V) land on the same XCD and share its L2. A bijection on [0, total).

@@ -137,10 +137,12 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(F
   const int q0 = qtile * kBM;
 
   const size_t head = (size_t)bh * N * D;
+  // Query head h attends with K/V head h / (H / Hkv).
+  const size_t kvhead = (size_t)((bh / a.H) * a.Hkv + (bh % a.H) / (a.H / a.Hkv)) * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * S::ES;
   const HeadBuf Q(reinterpret_cast<const T*>(a.q) + head, head_bytes);
-  const HeadBuf K(reinterpret_cast<const T*>(a.k) + head, head_bytes);
-  const HeadBuf V(reinterpret_cast<const T*>(a.v) + head, head_bytes);
+  const HeadBuf K(reinterpret_cast<const T*>(a.k) + kvhead, head_bytes);
+  const HeadBuf V(reinterpret_cast<const T*>(a.v) + kvhead, head_bytes);
   T* O = reinterpret_cast<T*>(a.o) + head;
   float* L = a.lse + (size_t)bh * N;
 
@@ -179,10 +181,14 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(F
     }
   }
 
-  // Key tiles this workgroup visits: all of them, or (causal) only those
-  // holding a key <= the last query row of the tile.
-  const int nkv_all = (N + kBN - 1) / kBN;
-  const int nkv = CAUSAL ? min(nkv_all, (min(q0 + kBM, N) - 1) / kBN + 1) : nkv_all;
+  // Key tiles t0 .. t0+nkv-1 this workgroup visits: those holding a key some
+  // of its rows can see (all of them, or fewer under the causal rule and a
+  // window); a wave computes on the tiles its own rows can see.
+  const int qlast = min(q0 + kBM, N) - 1;
+  const int t0 = first_visible_key(q0, a.wl) / kBN;
+  const int nkv = last_visible_key(qlast, N, CAUSAL, a.wr) / kBN - t0 + 1;
+  const int wk_lo = first_visible_key(qw0, a.wl);
+  const int wk_hi = last_visible_key(min(qw0 + 31, N - 1), N, CAUSAL, a.wr);
 
   const float c = a.scale_log2;  // scale * log2(e)
   // Reference max (raw scores) the exponentials are taken against; it only
@@ -204,14 +210,13 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(F
 #pragma unroll
       for (int i = 0; i < S::NQK; ++i) s[mt] = E::mma(ld<Raw>(kp + i * KH * S::ES), qf[i], s[mt]);
     }
-    if (need_mask) {  // diagonal or tail tile: hidden scores -> -inf (probability 0)
+    if (need_mask) {  // diagonal, window edge or tail: hidden scores -> -inf (probability 0)
 #pragma unroll
       for (int mt = 0; mt < S::NMT; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool vis = key < N && (!CAUSAL || key <= qrow);
-          if (!vis) s[mt][r] = -INFINITY;
+          if (!key_visible(key, qrow, N, CAUSAL, a.wl, a.wr)) s[mt][r] = -INFINITY;
         }
     }
     float mx = -INFINITY;
@@ -269,7 +274,7 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(F
   };
 
   TileLoader<T, D> tl;
-  tl.load(K, V, 0, tid);
+  tl.load(K, V, t0 * kBN, tid);
   tl.store(lds, tid);
 #pragma unroll
   for (int i = 0; i < S::NQK; ++i) settle(qf[i]);
@@ -277,10 +282,10 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(F
 
   for (int j = 0; j < nkv; ++j) {
     const char* stage = lds + (j & 1) * S::STAGE;
-    if (j + 1 < nkv) tl.load(K, V, (j + 1) * kBN, tid);
-    const int k0 = j * kBN;
-    if (wave_active && (!CAUSAL || k0 <= qw0 + 31)) {
-      tile(stage, k0, (CAUSAL && k0 + kBN - 1 > qw0) || (k0 + kBN > N));
+    if (j + 1 < nkv) tl.load(K, V, (t0 + j + 1) * kBN, tid);
+    const int k0 = (t0 + j) * kBN;
+    if (wave_active && k0 <= wk_hi && k0 + kBN - 1 >= wk_lo) {
+      tile(stage, k0, !block_all_visible(qw0, qw0 + 31, k0, k0 + kBN - 1, N, CAUSAL, a.wl, a.wr));
     }
     if (j + 1 < nkv) tl.store(lds + ((j + 1) & 1) * S::STAGE, tid);
     __syncthreads();
@@ -383,10 +388,12 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a) {
   const int q0 = qtile * kPPBM;
 
   const size_t head = (size_t)bh * N * D;
+  // Query head h attends with K/V head h / (H / Hkv).
+  const size_t kvhead = (size_t)((bh / a.H) * a.Hkv + (bh % a.H) / (a.H / a.Hkv)) * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const HeadBuf Q(reinterpret_cast<const T*>(a.q) + head, head_bytes);
-  const HeadBuf K(reinterpret_cast<const T*>(a.k) + head, head_bytes);
-  const HeadBuf V(reinterpret_cast<const T*>(a.v) + head, head_bytes);
+  const HeadBuf K(reinterpret_cast<const T*>(a.k) + kvhead, head_bytes);
+  const HeadBuf V(reinterpret_cast<const T*>(a.v) + kvhead, head_bytes);
   T* O = reinterpret_cast<T*>(a.o) + head;
   float* L = a.lse + (size_t)bh * N;
 
@@ -399,11 +406,18 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a) {
   const int qw0 = q0 + wave * 32;      // first query row of this wave
   const int qrow = qw0 + col;          // the query row this lane serves
 
-  // Key tiles: the workgroup streams those any of its rows can see; this
-  // wave computes on those its own rows can see.
-  const int nkv_all = (N + kBN - 1) / kBN;
-  const int nkv = CAUSAL ? min(nkv_all, (min(q0 + kPPBM, N) - 1) / kBN + 1) : nkv_all;
-  const int nkv_w = qw0 >= N ? 0 : CAUSAL ? min(nkv_all, (qw0 + 31) / kBN + 1) : nkv_all;
+  // Key tiles: the workgroup streams tiles t0 .. t0+nkv-1, those holding a
+  // key some of its rows can see (all of them, or fewer under the causal rule
+  // and a window); this wave computes on its steps [w_lo, w_end), the tiles
+  // its own rows can see (none if its rows are all past N).
+  const int qlast = min(q0 + kPPBM, N) - 1;
+  const int t0 = first_visible_key(q0, a.wl) / kBN;
+  const int nkv = last_visible_key(qlast, N, CAUSAL, a.wr) / kBN - t0 + 1;
+  int w_lo = nkv + 1, w_end = -1;
+  if (qw0 < N) {
+    w_lo = first_visible_key(qw0, a.wl) / kBN - t0;
+    w_end = last_visible_key(min(qw0 + 31, N - 1), N, CAUSAL, a.wr) / kBN - t0 + 1;
+  }
 
   // Q^T as MFMA B operands: lane half h holds head-dim elements
   // [h*D/2, h*D/2 + D/2) of its row, KH per MFMA.
@@ -505,15 +519,14 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a) {
 
   // Online softmax of one tile: scores s -> probabilities pf.
   auto softmax = [&](int k0) {
-    if ((CAUSAL && k0 + kBN - 1 > qw0) || k0 + kBN > N) {
-      // Diagonal or tail tile: hidden scores -> -inf (probability 0).
+    if (!block_all_visible(qw0, qw0 + 31, k0, k0 + kBN - 1, N, CAUSAL, a.wl, a.wr)) {
+      // Diagonal, window edge or tail tile: hidden scores -> -inf (probability 0).
 #pragma unroll
       for (int mt = 0; mt < S::NMT; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool vis = key < N && (!CAUSAL || key <= qrow);
-          if (!vis) s[mt][r] = -INFINITY;
+          if (!key_visible(key, qrow, N, CAUSAL, a.wl, a.wr)) s[mt][r] = -INFINITY;
         }
     }
     float mx = -INFINITY;
@@ -559,7 +572,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a) {
   using GS = GroupStage<D>;
   GS stg;
   if (group == 0 || nkv > 1) {
-    stg.load(K, group * kBN, gtid);
+    stg.load(K, (t0 + group) * kBN, gtid);
     stg.store(kbuf + group * S::K_BYTES, GS::k_off(gtid), GS::K_STRIDE);
   }
 #pragma unroll
@@ -580,32 +593,34 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a) {
   // Step 0 (no PV yet).
   {
     const int lt = kgrp ? 2 : 0;
-    if (lt < nkv) stg.load(X, lt * kBN, gtid);
-    if (nkv_w > 0) mphase(vbuf, kbuf, BoolC<false>{}, BoolC<true>{});
+    if (lt < nkv) stg.load(X, (t0 + lt) * kBN, gtid);
+    if (w_lo == 0 && w_end > 0) mphase(vbuf, kbuf, BoolC<false>{}, BoolC<true>{});
     __syncthreads();
-    if (nkv_w > 0) softmax(0);
+    if (w_lo == 0 && w_end > 0) softmax(t0 * kBN);
     if (lt < nkv) stg.store(kgrp ? kbuf : vbuf, soff, sstride);
     __syncthreads();
   }
-  // Steps 1 .. nkv-1, one code path: at step nkv_w (a causal wave past its
-  // last visible tile) only the PV half matters and the QK half is unused.
+  // Steps 1 .. nkv-1, one code path. At step w_lo (a wave whose first
+  // visible tile is not the workgroup's first) the PV half multiplies the
+  // previous V tile by probabilities that are still all zero, and at step
+  // w_end (a wave past its last visible tile) the QK half is unused.
   for (int i = 1; i < nkv; ++i) {
     const int lt = kgrp ? i + 2 : i;  // the tile this group streams
-    if (lt < nkv) stg.load(X, lt * kBN, gtid);
-    if (i <= nkv_w)
+    if (lt < nkv) stg.load(X, (t0 + lt) * kBN, gtid);
+    if (w_lo <= i && i <= w_end)
       mphase(vbuf + ((i - 1) & 1) * S::V_BYTES, kbuf + (i & 1) * S::K_BYTES, BoolC<true>{},
              BoolC<true>{});
     __syncthreads();
-    if (i < nkv_w) softmax(i * kBN);
+    if (w_lo <= i && i < w_end) softmax((t0 + i) * kBN);
     if (lt < nkv) stg.store(kgrp ? kbuf + (i & 1) * S::K_BYTES : vbuf + (i & 1) * S::V_BYTES, soff, sstride);
     __syncthreads();
   }
   // Final matrix phase: PV of the last tile.
-  if (nkv == nkv_w) mphase(vbuf + ((nkv - 1) & 1) * S::V_BYTES, kbuf, BoolC<true>{}, BoolC<false>{});
+  if (w_end == nkv) mphase(vbuf + ((nkv - 1) & 1) * S::V_BYTES, kbuf, BoolC<true>{}, BoolC<false>{});
   __syncthreads();
   if (!kgrp) __syncthreads();
 
-  if (nkv_w == 0 || qrow >= N) return;
+  if (w_end <= 0 || qrow >= N) return;
   const float lt = l + __shfl_xor(l, 32);
   const float inv = 1.0f / lt;
   T* orow = O + (size_t)qrow * D;

@@ -20,6 +20,8 @@ struct FwdArgs {
   float scale_log2;  // scale * log2(e)
   int causal;
   int dtype;         // fa_dtype
+  int Hkv;           // K/V heads (divides H)
+  int wl, wr;        // window bounds (negative: unbounded)
 };
 
 // Backward: forward tensors plus dO and the gradient outputs. `dsum` is the
@@ -41,6 +43,8 @@ struct BwdArgs {
   float scale_log2;
   int causal;
   int dtype;
+  int Hkv;     // K/V heads (divides H)
+  int wl, wr;  // window bounds (negative: unbounded)
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);

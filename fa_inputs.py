@@ -10,7 +10,7 @@ Recipe (the same for every workload):
   * float32 standard-normal draws in the fixed order Q, K, V, then dO when a
     backward pass is needed, each of shape [B, H, N, d] (batch, heads,
     sequence, head dim -- the layout in which the tutorial page's code unpacks
-    ``q.shape``);
+    ``q.shape``); with grouped K/V heads, K and V are [B, Hkv, N, d];
   * an optional multiplication by ``input_scale`` (0.5 for the B=4 H=16
     N=4096 workload; a power of two, so it commutes exactly with rounding);
   * a round-to-nearest-even cast to the workload's dtype (torch's cast).
@@ -76,21 +76,24 @@ WORKLOADS = {
 
 
 def make_inputs(B: int, H: int, N: int, d: int, dtype: str, *, seed: int = 0,
-                input_scale: float = 1.0, backward: bool = False) -> dict:
+                input_scale: float = 1.0, backward: bool = False,
+                kv_heads: int | None = None) -> dict:
     """Draw Q, K, V (and dO) on the CPU following the recipe above.
 
     Returns a dict of contiguous CPU tensors of the requested dtype with keys
-    ``q``, ``k``, ``v`` and, when ``backward``, ``do``.
+    ``q``, ``k``, ``v`` and, when ``backward``, ``do``. ``kv_heads`` (default
+    H) is the head count of K and V.
     """
     if dtype not in _DTYPES:
         raise ValueError(f"unknown dtype {dtype!r}")
     g = torch.Generator(device="cpu")
     g.manual_seed(seed)
-    shape = (B, H, N, d)
+    hkv = H if kv_heads is None else kv_heads
+    shapes = {"q": (B, H, N, d), "k": (B, hkv, N, d), "v": (B, hkv, N, d), "do": (B, H, N, d)}
     names = ["q", "k", "v"] + (["do"] if backward else [])
     out = {}
     for name in names:
-        x = torch.randn(shape, generator=g, dtype=torch.float32)
+        x = torch.randn(shapes[name], generator=g, dtype=torch.float32)
         if input_scale != 1.0:
             x = x * input_scale
         out[name] = x.to(_DTYPES[dtype]).contiguous()

@@ -124,6 +124,53 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            int B, int H, int N, int d, float scale, int causal, int dtype,
            void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Variants: grouped K/V heads and local windows.
+ *
+ * fa_options selects two generalizations of the operation above. Both
+ * reduce to it with kv_heads = 0 (or H) and both window bounds negative.
+ *   kv_heads     : Hkv, the number of K/V heads (multi-query / grouped-query
+ *                  attention). It must divide H; 0 means H. K, V (and in the
+ *                  backward dK, dV) are then [B, Hkv, N, d]. Query head h
+ *                  attends with K/V head h / (H / Hkv), and dK, dV of a K/V
+ *                  head are the sums over the query heads that use it.
+ *   window_left  : >= 0: key j is hidden from query i if j < i - window_left.
+ *                  Negative: no bound on that side.
+ *   window_right : >= 0: key j is hidden from query i if j > i + window_right.
+ *                  Negative: no bound on that side. The window combines with
+ *                  ``causal`` (causal alone is the window (unbounded, 0)).
+ * Every query row sees at least its own key (a non-negative bound never
+ * excludes j = i). Key tiles that lie entirely outside every query's window
+ * are never visited: they generalize the causal tile skipping of the pages'
+ * section 二.7 to a band.
+ */
+typedef struct fa_options {
+  int kv_heads;
+  int window_left;
+  int window_right;
+} fa_options;
+
+/*
+ * fa_fwd_ex -- fa_fwd with options (``opts`` may be NULL: plain attention).
+ * k and v are [B, Hkv, N, d]; everything else as for fa_fwd. Validation adds:
+ * kv_heads < 0, or not dividing H -> FA_ERR_INVALID_ARG.
+ */
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int H, int N, int d, float scale, int causal, int dtype,
+              const fa_options* opts, void* stream);
+
+/*
+ * fa_bwd_ex -- fa_bwd with options (``opts`` may be NULL). k, v, dk, dv are
+ * [B, Hkv, N, d]; the workspace size is fa_bwd_workspace_size(B, H, N, d)
+ * (it depends on the query heads only). scale, causal and opts must match
+ * the forward call that produced o and lse.
+ */
+int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
+              const void* dO, const float* lse, void* dq, void* dk, void* dv,
+              int B, int H, int N, int d, float scale, int causal, int dtype,
+              const fa_options* opts, void* workspace, size_t workspace_bytes,
+              void* stream);
+
 /* fa_strerror -- static, NUL-terminated description of a status code. */
 const char* fa_strerror(int status);
 

@@ -26,7 +26,8 @@ def lib():
 
 def test_header_functions_are_exported(lib):
     names = _lib.header_functions()
-    assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_strerror"}
+    assert set(names) == {"fa_fwd", "fa_bwd", "fa_fwd_ex", "fa_bwd_ex", "fa_bwd_workspace_size",
+                          "fa_strerror"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -126,3 +127,61 @@ def test_library_is_native_shared_object():
     with open(_lib.LIB_PATH, "rb") as f:
         assert f.read(4) == b"\x7fELF"
     assert isinstance(_lib.load(), ctypes.CDLL)
+
+
+def fwd_ex(lib, kv_heads=0, wl=-1, wr=-1, opts=True, q=Q, k=K, v=V, o=O, lse=LSE, B=1, H=4,
+           N=16, d=64, causal=0, dtype=2):
+    op = ctypes.byref(_lib.FaOptions(kv_heads, wl, wr)) if opts else None
+    return lib.fa_fwd_ex(q, k, v, o, lse, B, H, N, d, 0.125, causal, dtype, op, None)
+
+
+def bwd_ex(lib, kv_heads=0, wl=-1, wr=-1, q=Q, k=K, v=V, o=O, dq=DQ, dk=DK, B=1, H=4, N=16,
+           d=64, causal=1, dtype=1):
+    op = ctypes.byref(_lib.FaOptions(kv_heads, wl, wr))
+    ws = lib.fa_bwd_workspace_size(B, H, N, d)
+    return lib.fa_bwd_ex(q, k, v, o, DO, LSE, dq, dk, DV, B, H, N, d, 0.125, causal, dtype, op,
+                         WS, ws, None)
+
+
+KV_BYTES_1 = 1 * 1 * 16 * 64 * 2  # one K/V head of the calls above (bf16)
+
+FWD_EX_CASES = [
+    (dict(kv_heads=-1), FA_ERR_INVALID_ARG),
+    (dict(kv_heads=3), FA_ERR_INVALID_ARG),                 # does not divide H=4
+    (dict(kv_heads=8), FA_ERR_INVALID_ARG),                 # more K/V heads than query heads
+    (dict(kv_heads=2, q=None), FA_ERR_INVALID_ARG),
+    (dict(kv_heads=2, d=80), FA_ERR_UNSUPPORTED),
+    (dict(kv_heads=2, causal=3), FA_ERR_INVALID_ARG),
+    (dict(wl=5, k=K + 8), FA_ERR_ALIGN),
+    # With one K/V head, k spans KV_BYTES_1 bytes: an output starting inside
+    # it overlaps, one starting right past it would not.
+    (dict(kv_heads=1, o=K + KV_BYTES_1 - 256), FA_ERR_INVALID_ARG),
+    (dict(kv_heads=1, lse=V + KV_BYTES_1 - 256), FA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("kw,status", FWD_EX_CASES)
+def test_fwd_ex_rejects(lib, kw, status):
+    assert fwd_ex(lib, **kw) == status
+
+
+BWD_EX_CASES = [
+    (dict(kv_heads=-2), FA_ERR_INVALID_ARG),
+    (dict(kv_heads=3), FA_ERR_INVALID_ARG),
+    (dict(kv_heads=2, wl=4, d=32), FA_ERR_UNSUPPORTED),
+    (dict(kv_heads=2, dk=DK + 2), FA_ERR_ALIGN),
+    (dict(kv_heads=1, dk=K + KV_BYTES_1 - 256), FA_ERR_INVALID_ARG),  # dk overlaps k
+    (dict(kv_heads=2, dq=O), FA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("kw,status", BWD_EX_CASES)
+def test_bwd_ex_rejects(lib, kw, status):
+    assert bwd_ex(lib, **kw) == status
+
+
+def test_ex_with_null_options_validates_like_plain(lib):
+    # NULL options = plain attention; the same single defects are rejected.
+    assert fwd_ex(lib, opts=False, q=None) == FA_ERR_INVALID_ARG
+    assert fwd_ex(lib, opts=False, d=96) == FA_ERR_UNSUPPORTED
+    assert fwd_ex(lib, opts=False, o=O + 2) == FA_ERR_ALIGN
