@@ -23,6 +23,7 @@ import torch
 from . import _lib
 
 __all__ = ["FaError", "fa_fwd", "fa_bwd", "fa_fwd_ex", "fa_bwd_ex", "fa_bwd_workspace_size",
+           "fa_fwd_num_splits", "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv",
            "fa_strerror", "forward", "backward", "DTYPES"]
 
 DTYPES = {torch.float32: _lib.FA_F32, torch.float16: _lib.FA_F16,
@@ -152,6 +153,40 @@ def fa_bwd_ex(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool, works
         raise FaError(st, "fa_bwd_ex")
 
 
+def fa_fwd_num_splits(B: int, H: int, N: int, d: int, dtype) -> int:
+    """Split count fa_fwd_splitkv picks for num_splits=0 (dtype: torch dtype)."""
+    return int(_lib.load().fa_fwd_num_splits(B, H, N, d, DTYPES[dtype]))
+
+
+def fa_fwd_splitkv_workspace_size(B: int, H: int, N: int, d: int, dtype,
+                                  num_splits: int = 0) -> int:
+    return int(_lib.load().fa_fwd_splitkv_workspace_size(B, H, N, d, DTYPES[dtype],
+                                                         num_splits))
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, scale: float, causal: bool, num_splits: int, workspace,
+                   window=None, stream=None) -> None:
+    """fa_fwd_ex computed with split-KV: the key tiles of every query tile in
+    ``num_splits`` slices (0 = the library's choice), merged afterwards.
+    ``workspace`` may be None when fa_fwd_splitkv_workspace_size is 0."""
+    B, H, Hkv, N, d = _kv_shape(q, k)
+    _check({"q": q, "o": o}, (B, H, N, d), q.dtype)
+    _check({"k": k, "v": v}, (B, Hkv, N, d), q.dtype)
+    _check({"lse": lse}, (B, H, N), torch.float32)
+    if workspace is not None and (not workspace.is_cuda or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    opts = _options(Hkv, window)
+    with torch.cuda.device(q.device):
+        st = _lib.load().fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                        lse.data_ptr(), B, H, N, d, float(scale),
+                                        int(bool(causal)), DTYPES[q.dtype], ctypes.byref(opts),
+                                        int(num_splits), ws_ptr, ws_bytes, _stream(q, stream))
+    if st != _lib.FA_OK:
+        raise FaError(st, "fa_fwd_splitkv")
+
+
 def _plain(q, k, window) -> bool:
     return window is None and k.dim() == 4 and k.shape[1] == q.shape[1]
 
@@ -161,13 +196,19 @@ def _default_scale(d: int, scale):
 
 
 def forward(q, k, v, causal: bool = False, scale: float | None = None, stream=None,
-            window=None):
+            window=None, num_splits: int | None = None):
     """Allocate O and LSE with torch and run fa_fwd (fa_fwd_ex when k, v have
-    fewer heads than q or a window is given); returns (o, lse)."""
+    fewer heads than q or a window is given; fa_fwd_splitkv, with a workspace
+    allocated here, when ``num_splits`` is given); returns (o, lse)."""
     B, H, N, d = _shape(q)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if _plain(q, k, window):
+    if num_splits is not None:
+        nbytes = fa_fwd_splitkv_workspace_size(B, H, N, d, q.dtype, num_splits)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
+        fa_fwd_splitkv(q, k, v, o, lse, _default_scale(d, scale), causal, num_splits, ws,
+                       window, stream)
+    elif _plain(q, k, window):
         fa_fwd(q, k, v, o, lse, _default_scale(d, scale), causal, stream)
     else:
         fa_fwd_ex(q, k, v, o, lse, _default_scale(d, scale), causal, window, stream)

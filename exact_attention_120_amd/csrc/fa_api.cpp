@@ -32,6 +32,7 @@ bool overlap(const void* p, size_t n, const void* q, size_t m) {
 }
 
 constexpr size_t kAlign = 256;
+constexpr int kMaxSplits = 64;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Shared shape checks. Returns FA_OK or the status to report.
@@ -98,6 +99,64 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
            int N, int d, float scale, int causal, int dtype, void* stream) {
   return fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, nullptr, stream);
+}
+
+int fa_fwd_num_splits(int B, int H, int N, int d, int dtype) {
+  if (check_shape(B, H, N, d, 1.f, 0, dtype) != FA_OK) return 0;
+  return fa::fwd_auto_splits(B, H, N, dtype);
+}
+
+size_t fa_fwd_splitkv_workspace_size(int B, int H, int N, int d, int dtype, int num_splits) {
+  if (check_shape(B, H, N, d, 1.f, 0, dtype) != FA_OK) return 0;
+  if (num_splits < 0 || num_splits > kMaxSplits) return 0;
+  const int s = num_splits == 0 ? fa::fwd_auto_splits(B, H, N, dtype) : num_splits;
+  if (s == 1) return 0;
+  const size_t rows = (size_t)s * B * H * N;
+  return round_up(rows * d * sizeof(float)) + round_up(rows * sizeof(float));
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                   int H, int N, int d, float scale, int causal, int dtype,
+                   const fa_options* opts, int num_splits, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  int st = check_shape(B, H, N, d, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  Opts op;
+  if ((st = read_opts(opts, H, &op)) != FA_OK) return st;
+  if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_INVALID_ARG;
+  const int ns = num_splits == 0 ? fa::fwd_auto_splits(B, H, N, dtype) : num_splits;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  const size_t need = fa_fwd_splitkv_workspace_size(B, H, N, d, dtype, ns);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return FA_ERR_ALIGN;
+  }
+  const size_t tb = (size_t)B * H * N * d * elem_size(dtype);
+  const size_t kb = (size_t)B * op.Hkv * N * d * elem_size(dtype);
+  const size_t lb = (size_t)B * H * N * sizeof(float);
+  struct Range { const void* p; size_t n; };
+  const Range ins[] = {{q, tb}, {k, kb}, {v, kb}};
+  const Range outs[] = {{o, tb}, {lse, lb}, {workspace, need}};
+  for (const Range& w : outs) {
+    if (w.n == 0) continue;
+    for (const Range& r : ins)
+      if (overlap(w.p, w.n, r.p, r.n)) return FA_ERR_INVALID_ARG;
+    for (const Range& x : outs)
+      if (&x != &w && x.n > 0 && overlap(w.p, w.n, x.p, x.n)) return FA_ERR_INVALID_ARG;
+  }
+  if (fa::fwd_grid_size(B, H, N) * ns >= (1ll << 31)) return FA_ERR_UNSUPPORTED;
+
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, exp2_scale(scale), causal, dtype,
+                op.Hkv, op.wl, op.wr};
+  if (ns > 1) {
+    char* ws = static_cast<char*>(workspace);
+    a.num_splits = ns;
+    a.o_part = reinterpret_cast<float*>(ws);
+    a.lse_part = reinterpret_cast<float*>(ws + round_up((size_t)ns * B * H * N * d * sizeof(float)));
+  }
+  return hip_status(fa::launch_fwd(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {

@@ -50,6 +50,39 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kBM = kWaves * 32;  // query rows per workgroup
 constexpr int kBN = 64;           // keys per K/V tile
 
+// Split-KV: slice `split` of `nsplit` of the key tiles [t0, t0 + nkv), an
+// even share in order (empty when there are more slices than tiles).
+__device__ inline void split_slice(int split, int nsplit, int& t0, int& nkv) {
+  if (nsplit == 1) return;
+  const int a0 = split * nkv / nsplit, a1 = (split + 1) * nkv / nsplit;
+  t0 += a0;
+  nkv = a1 - a0;
+}
+
+// One row's split-KV partial (this lane's half of the head dim, in the
+// accumulator layout of the epilogues): O normalized over the slice's keys,
+// in float32, and the slice's LSE. A row that saw no key of the slice
+// (lt == 0) gets O = 0 and LSE = -inf, which the merge weighs with
+// exp(-inf) = 0.
+template <int NDT>
+__device__ inline void write_partial(const FwdArgs& a, int split, int bh, int qrow, int half,
+                                     const f32x16 (&o)[NDT], float m, float lt) {
+  constexpr int D = NDT * 32;
+  const size_t rows = (size_t)a.B * a.H * a.N;
+  const size_t row = (size_t)split * rows + (size_t)bh * a.N + qrow;
+  const bool empty = !(lt > 0.f);
+  const float inv = empty ? 0.f : 1.0f / lt;
+  float* orow = a.o_part + row * D;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      st<f32x4>(orow + dt * 32 + 8 * g + 4 * half,
+                f32x4{o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv, o[dt][4 * g + 2] * inv,
+                      o[dt][4 * g + 3] * inv});
+  if (half == 0) a.lse_part[row] = empty ? -INFINITY : m * a.scale + logf(lt);
+}
+
 template <typename T, int D>
 struct FwdShape {
   using E = Elem<T>;
@@ -132,8 +165,10 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(F
   const int N = a.N;
   const int nqt = (N + kBM - 1) / kBM;
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = lin / nqt;
-  const int qtile = CAUSAL ? nqt - 1 - lin % nqt : lin % nqt;
+  const int nsplit = a.num_splits;
+  const int bh = lin / (nqt * nsplit);
+  const int qi = lin % (nqt * nsplit) / nsplit, split = lin % nsplit;
+  const int qtile = CAUSAL ? nqt - 1 - qi : qi;
   const int q0 = qtile * kBM;
 
   const size_t head = (size_t)bh * N * D;
@@ -183,10 +218,12 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(F
 
   // Key tiles t0 .. t0+nkv-1 this workgroup visits: those holding a key some
   // of its rows can see (all of them, or fewer under the causal rule and a
-  // window); a wave computes on the tiles its own rows can see.
+  // window), or its slice of them under split-KV; a wave computes on the
+  // tiles its own rows can see.
   const int qlast = min(q0 + kBM, N) - 1;
-  const int t0 = first_visible_key(q0, a.wl) / kBN;
-  const int nkv = last_visible_key(qlast, N, CAUSAL, a.wr) / kBN - t0 + 1;
+  int t0 = first_visible_key(q0, a.wl) / kBN;
+  int nkv = last_visible_key(qlast, N, CAUSAL, a.wr) / kBN - t0 + 1;
+  split_slice(split, nsplit, t0, nkv);
   const int wk_lo = first_visible_key(qw0, a.wl);
   const int wk_hi = last_visible_key(min(qw0 + 31, N - 1), N, CAUSAL, a.wr);
 
@@ -273,6 +310,10 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(F
     }
   };
 
+  if (nkv == 0) {  // an empty slice: nothing to visit, an empty partial
+    if (wave_active && qrow < N) write_partial(a, split, bh, qrow, half, o, -FLT_MAX, 0.f);
+    return;
+  }
   TileLoader<T, D> tl;
   tl.load(K, V, t0 * kBN, tid);
   tl.store(lds, tid);
@@ -293,6 +334,10 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(F
 
   if (!wave_active || qrow >= N) return;
   const float lt = l + __shfl_xor(l, 32);
+  if (nsplit > 1) {
+    write_partial(a, split, bh, qrow, half, o, m, lt);
+    return;
+  }
   const float inv = 1.0f / lt;
   T* orow = O + (size_t)qrow * D;
 #pragma unroll
@@ -383,8 +428,10 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a) {
   const int N = a.N;
   const int nqt = (N + kPPBM - 1) / kPPBM;
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = lin / nqt;
-  const int qtile = CAUSAL ? nqt - 1 - lin % nqt : lin % nqt;
+  const int nsplit = a.num_splits;
+  const int bh = lin / (nqt * nsplit);
+  const int qi = lin % (nqt * nsplit) / nsplit, split = lin % nsplit;
+  const int qtile = CAUSAL ? nqt - 1 - qi : qi;
   const int q0 = qtile * kPPBM;
 
   const size_t head = (size_t)bh * N * D;
@@ -408,15 +455,18 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a) {
 
   // Key tiles: the workgroup streams tiles t0 .. t0+nkv-1, those holding a
   // key some of its rows can see (all of them, or fewer under the causal rule
-  // and a window); this wave computes on its steps [w_lo, w_end), the tiles
-  // its own rows can see (none if its rows are all past N).
+  // and a window), or its slice of them under split-KV; this wave computes on
+  // its steps [w_lo, w_end), the tiles its own rows can see (none if its rows
+  // are all past N or see no key of the slice).
   const int qlast = min(q0 + kPPBM, N) - 1;
-  const int t0 = first_visible_key(q0, a.wl) / kBN;
-  const int nkv = last_visible_key(qlast, N, CAUSAL, a.wr) / kBN - t0 + 1;
+  int t0 = first_visible_key(q0, a.wl) / kBN;
+  int nkv = last_visible_key(qlast, N, CAUSAL, a.wr) / kBN - t0 + 1;
+  split_slice(split, nsplit, t0, nkv);
   int w_lo = nkv + 1, w_end = -1;
   if (qw0 < N) {
-    w_lo = first_visible_key(qw0, a.wl) / kBN - t0;
-    w_end = last_visible_key(min(qw0 + 31, N - 1), N, CAUSAL, a.wr) / kBN - t0 + 1;
+    const int lo = max(first_visible_key(qw0, a.wl) / kBN - t0, 0);
+    const int hi = min(last_visible_key(min(qw0 + 31, N - 1), N, CAUSAL, a.wr) / kBN - t0 + 1, nkv);
+    if (lo < hi) w_lo = lo, w_end = hi;
   }
 
   // Q^T as MFMA B operands: lane half h holds head-dim elements
@@ -568,6 +618,11 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a) {
       }
   };
 
+  if (nkv == 0) {  // an empty slice: nothing to visit, an empty partial
+    if (qrow < N) write_partial(a, split, bh, qrow, half, o, -FLT_MAX, 0.f);
+    return;
+  }
+
   // Prologue: K tiles 0 and 1 (group A stages tile 0, group B tile 1).
   using GS = GroupStage<D>;
   GS stg;
@@ -620,8 +675,12 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a) {
   __syncthreads();
   if (!kgrp) __syncthreads();
 
-  if (w_end <= 0 || qrow >= N) return;
+  if (qrow >= N) return;
   const float lt = l + __shfl_xor(l, 32);
+  if (nsplit > 1) {
+    write_partial(a, split, bh, qrow, half, o, m, lt);
+    return;
+  }
   const float inv = 1.0f / lt;
   T* orow = O + (size_t)qrow * D;
 #pragma unroll
@@ -636,12 +695,50 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a) {
   if (half == 0) L[qrow] = m * a.scale + logf(lt);
 }
 
+// Split-KV merge of the partials of every row: with M = max_s LSE_s and
+// w_s = exp(LSE_s - M), O = sum_s w_s O_s / sum_s w_s and
+// LSE = M + ln(sum_s w_s) -- the softmax over the union of the slices' keys,
+// rebuilt from each slice's normalized output and normalizer. D/4 threads
+// per row, 4 head-dim columns each.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void fwd_merge_kernel(FwdArgs a) {
+  constexpr int TPR = D / 4;
+  constexpr int RPB = 256 / TPR;
+  const long long rows = (long long)a.B * a.H * a.N;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+  if (row >= rows) return;
+  const int c = (threadIdx.x % TPR) * 4;
+  const int ns = a.num_splits;
+  float mx = -INFINITY;
+  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, a.lse_part[s * rows + row]);
+  const float mref = mx == -INFINITY ? 0.f : mx;
+  float den = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < ns; ++s) {
+    const float w = __builtin_amdgcn_exp2f((a.lse_part[s * rows + row] - mref) * kLog2e);
+    const f32x4 x = ld<f32x4>(a.o_part + ((size_t)s * rows + row) * D + c);
+    den += w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, x[e], acc[e]);
+  }
+  const float inv = den > 0.f ? 1.0f / den : 0.f;
+  T* orow = reinterpret_cast<T*>(a.o) + row * D + c;
+  if constexpr (sizeof(T) == 2) {
+    using E = Elem<T>;
+    st<u32x2>(orow, u32x2{E::bits(acc[0] * inv) | ((uint32_t)E::bits(acc[1] * inv) << 16),
+                          E::bits(acc[2] * inv) | ((uint32_t)E::bits(acc[3] * inv) << 16)});
+  } else {
+    st<f32x4>(orow, f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv});
+  }
+  if (c == 0) a.lse[row] = den > 0.f ? mref + logf(den) : -INFINITY;
+}
+
 template <typename T, int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   constexpr bool kPP = sizeof(T) == 2;
   const int bm = kPP ? kPPBM : kBM;
   const int nqt = (a.N + bm - 1) / bm;
-  const dim3 grid((unsigned)((long long)a.B * a.H * nqt));
+  const dim3 grid((unsigned)((long long)a.B * a.H * nqt * a.num_splits));
   FwdArgs args = a;
   void* kargs[] = {&args};
   const void* fn;
@@ -649,7 +746,12 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
     fn = reinterpret_cast<const void*>(&fwd_pp_kernel<T, D, CAUSAL>);
   else
     fn = reinterpret_cast<const void*>(&fwd_kernel<T, D, CAUSAL>);
-  return hipLaunchKernel(fn, grid, dim3(kPP ? kPPThreads : kThreads), kargs, 0, stream);
+  hipError_t e = hipLaunchKernel(fn, grid, dim3(kPP ? kPPThreads : kThreads), kargs, 0, stream);
+  if (e != hipSuccess || a.num_splits == 1) return e;
+  constexpr int RPB = 256 / (D / 4);
+  const long long rows = (long long)a.B * a.H * a.N;
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_merge_kernel<T, D>),
+                         dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), kargs, 0, stream);
 }
 
 template <typename T>
@@ -662,6 +764,18 @@ hipError_t dispatch_d(const FwdArgs& a, hipStream_t s) {
 
 long long fwd_grid_size(int B, int H, int N) {
   return (long long)B * H * ((N + kBM - 1) / kBM);
+}
+
+int fwd_rows_per_workgroup(int dtype) { return dtype == 0 ? kBM : kPPBM; }
+
+int fwd_auto_splits(int B, int H, int N, int dtype) {
+  constexpr int kCUs = 256;
+  const int bm = fwd_rows_per_workgroup(dtype);
+  const long long wgs = (long long)B * H * ((N + bm - 1) / bm);
+  const int nkt = (N + kBN - 1) / kBN;
+  int s = 1;
+  while (s < 16 && wgs * s < kCUs && nkt / (2 * s) >= 4) s *= 2;
+  return s;
 }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {

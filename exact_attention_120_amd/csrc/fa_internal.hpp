@@ -22,6 +22,14 @@ struct FwdArgs {
   int dtype;         // fa_dtype
   int Hkv;           // K/V heads (divides H)
   int wl, wr;        // window bounds (negative: unbounded)
+  // Split-KV: with num_splits > 1 every workgroup covers one of num_splits
+  // slices of its key tiles and writes float32 partials -- O normalized over
+  // its slice's keys into o_part [num_splits][B,H,N,d] and that slice's LSE
+  // (-inf where a row sees none of its keys) into lse_part
+  // [num_splits][B,H,N] -- and a second kernel merges them into o and lse.
+  int num_splits = 1;
+  float* o_part = nullptr;
+  float* lse_part = nullptr;
 };
 
 // Backward: forward tensors plus dO and the gradient outputs. `dsum` is the
@@ -51,5 +59,11 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 
 long long fwd_grid_size(int B, int H, int N);
+
+// Rows per forward workgroup and the split count the library picks for a
+// shape: enough workgroups to occupy every compute unit once, with at least
+// four 64-key tiles per slice, at most 16 slices.
+int fwd_rows_per_workgroup(int dtype);
+int fwd_auto_splits(int B, int H, int N, int dtype);
 
 }  // namespace fa

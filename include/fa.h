@@ -171,6 +171,57 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
               const fa_options* opts, void* workspace, size_t workspace_bytes,
               void* stream);
 
+/*
+ * Split-KV forward.
+ *
+ * fa_fwd launches one workgroup per query tile of every head, so a short
+ * sequence with few heads leaves most compute units idle. fa_fwd_splitkv
+ * also splits the key tiles each query tile visits into ``num_splits``
+ * contiguous slices, one workgroup each. A slice's workgroup runs the same
+ * online softmax over its keys only and writes a float32 partial: O
+ * normalized over those keys, and their LSE (-inf for a row that sees none
+ * of them). A second kernel then merges the partials of each row with
+ * M = max_s LSE_s and w_s = exp(LSE_s - M): O = sum_s w_s O_s / sum_s w_s,
+ * LSE = M + ln(sum_s w_s). This is the blockwise softmax combination of the
+ * pages' sections 二.5/二.6, taken across workgroups instead of across the
+ * steps of one loop; the results equal fa_fwd_ex's up to float rounding.
+ */
+
+/*
+ * fa_fwd_num_splits -- the slice count fa_fwd_splitkv uses when called with
+ * num_splits = 0: the smallest power of two (at most 16) that gives every
+ * compute unit a workgroup, while each slice keeps at least four 64-key
+ * tiles. 1 means no split. Returns 0 for invalid sizes or dtype.
+ */
+int fa_fwd_num_splits(int B, int H, int N, int d, int dtype);
+
+/*
+ * fa_fwd_splitkv_workspace_size -- bytes of device workspace fa_fwd_splitkv
+ * needs with ``num_splits`` slices (0: the count fa_fwd_num_splits picks):
+ * float32 partial outputs [S, B, H, N, d] and partial LSE [S, B, H, N],
+ * each 256-byte aligned. 0 when S is 1 (no workspace is used) or for
+ * invalid arguments.
+ */
+size_t fa_fwd_splitkv_workspace_size(int B, int H, int N, int d, int dtype, int num_splits);
+
+/*
+ * fa_fwd_splitkv -- fa_fwd_ex computed with split-KV (see above).
+ *   num_splits : 1..64 slices, or 0 for fa_fwd_num_splits' choice. With 1 it
+ *                is exactly fa_fwd_ex.
+ *   workspace  : device scratch of at least fa_fwd_splitkv_workspace_size()
+ *                bytes for the same arguments, 256-byte aligned, owned by the
+ *                caller; contents on entry are ignored and undefined on exit.
+ *                May be NULL when that size is 0.
+ *   other arguments as for fa_fwd_ex (opts may be NULL).
+ * Validation adds: num_splits outside 0..64 -> FA_ERR_INVALID_ARG; workspace
+ * NULL or too small while one is needed -> FA_ERR_WORKSPACE; workspace
+ * overlapping an input or output -> FA_ERR_INVALID_ARG.
+ */
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, float scale, int causal, int dtype,
+                   const fa_options* opts, int num_splits, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
 /* fa_strerror -- static, NUL-terminated description of a status code. */
 const char* fa_strerror(int status);
 

@@ -27,6 +27,7 @@ def lib():
 def test_header_functions_are_exported(lib):
     names = _lib.header_functions()
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_fwd_ex", "fa_bwd_ex", "fa_bwd_workspace_size",
+                          "fa_fwd_num_splits", "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv",
                           "fa_strerror"}
     for n in names:
         assert hasattr(lib, n), n
@@ -185,3 +186,65 @@ def test_ex_with_null_options_validates_like_plain(lib):
     assert fwd_ex(lib, opts=False, q=None) == FA_ERR_INVALID_ARG
     assert fwd_ex(lib, opts=False, d=96) == FA_ERR_UNSUPPORTED
     assert fwd_ex(lib, opts=False, o=O + 2) == FA_ERR_ALIGN
+
+
+def test_num_splits_choice(lib):
+    # B=2, H=8, N=1024, bf16: 2*8*4 = 64 workgroups of 256 rows -> 4 slices
+    # of the 16 key tiles give 256 workgroups.
+    assert lib.fa_fwd_num_splits(2, 8, 1024, 64, 2) == 4
+    # Enough workgroups already: no split.
+    assert lib.fa_fwd_num_splits(1, 16, 16384, 128, 2) == 1
+    assert lib.fa_fwd_num_splits(4, 16, 4096, 128, 2) == 1
+    # Too few key tiles to split (N=128: two tiles).
+    assert lib.fa_fwd_num_splits(1, 1, 128, 64, 0) == 1
+    # One head, N=4096 (64 key tiles, 16 query tiles): 16 slices.
+    assert lib.fa_fwd_num_splits(1, 1, 4096, 128, 1) == 16
+    # Invalid arguments.
+    assert lib.fa_fwd_num_splits(0, 1, 128, 64, 2) == 0
+    assert lib.fa_fwd_num_splits(1, 1, 128, 80, 2) == 0
+    assert lib.fa_fwd_num_splits(1, 1, 128, 64, 9) == 0
+
+
+def test_splitkv_workspace_size(lib):
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    B, H, N, d = 2, 8, 1024, 64
+    for s in (2, 3, 64):
+        rows = s * B * H * N
+        assert lib.fa_fwd_splitkv_workspace_size(B, H, N, d, 2, s) == up(rows * d * 4) + up(rows * 4)
+    # 0 = the library's count (4 here).
+    assert (lib.fa_fwd_splitkv_workspace_size(B, H, N, d, 2, 0)
+            == lib.fa_fwd_splitkv_workspace_size(B, H, N, d, 2, 4))
+    assert lib.fa_fwd_splitkv_workspace_size(B, H, N, d, 2, 1) == 0
+    assert lib.fa_fwd_splitkv_workspace_size(1, 16, 16384, 128, 2, 0) == 0
+    assert lib.fa_fwd_splitkv_workspace_size(B, H, N, d, 2, 65) == 0
+    assert lib.fa_fwd_splitkv_workspace_size(B, H, N, d, 2, -1) == 0
+
+
+def splitkv(lib, num_splits=4, ws=WS, ws_bytes=None, kv_heads=0, q=Q, o=O, lse=LSE, B=2, H=8,
+            N=1024, d=64, dtype=2):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_fwd_splitkv_workspace_size(B, H, N, d, dtype, num_splits)
+    op = ctypes.byref(_lib.FaOptions(kv_heads, -1, -1))
+    return lib.fa_fwd_splitkv(q, K, V, o, lse, B, H, N, d, 0.125, 1, dtype, op, num_splits, ws,
+                              ws_bytes, None)
+
+
+SPLITKV_CASES = [
+    (dict(num_splits=-1), FA_ERR_INVALID_ARG),
+    (dict(num_splits=65), FA_ERR_INVALID_ARG),
+    (dict(ws=None), FA_ERR_WORKSPACE),
+    (dict(ws_bytes=4096), FA_ERR_WORKSPACE),
+    (dict(num_splits=0, ws_bytes=4096), FA_ERR_WORKSPACE),  # 0 -> 4 slices need space
+    (dict(ws=WS + 64), FA_ERR_ALIGN),
+    (dict(ws=Q), FA_ERR_INVALID_ARG),                       # workspace overlaps q
+    (dict(ws=O + 512), FA_ERR_INVALID_ARG),                 # workspace overlaps o
+    (dict(kv_heads=3), FA_ERR_INVALID_ARG),
+    (dict(q=None), FA_ERR_INVALID_ARG),
+    (dict(d=32), FA_ERR_UNSUPPORTED),
+    (dict(lse=LSE + 4), FA_ERR_ALIGN),
+]
+
+
+@pytest.mark.parametrize("kw,status", SPLITKV_CASES)
+def test_splitkv_rejects(lib, kw, status):
+    assert splitkv(lib, **kw) == status
