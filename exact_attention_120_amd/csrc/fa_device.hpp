@@ -65,6 +65,11 @@ struct Elem<__bf16> {
     acc += a + b;
     return __builtin_bit_cast(uint32_t, pr);
   }
+  // The packed word of (a, b) alone.
+  __device__ static inline uint32_t pack_pair(float a, float b) {
+    const bf16x2 pr = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, pr);
+  }
   __device__ static inline uint16_t bits(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
   }
@@ -96,6 +101,10 @@ struct Elem<_Float16> {
     const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
     const f16x2 pr = {(_Float16)a, (_Float16)b};
     acc = __builtin_amdgcn_fdot2(pr, one, acc, false);
+    return __builtin_bit_cast(uint32_t, pr);
+  }
+  __device__ static inline uint32_t pack_pair(float a, float b) {
+    const f16x2 pr = {(_Float16)a, (_Float16)b};
     return __builtin_bit_cast(uint32_t, pr);
   }
   __device__ static inline uint16_t bits(float x) {

@@ -579,14 +579,43 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a) {
           if (!key_visible(key, qrow, N, CAUSAL, a.wl, a.wr)) s[mt][r] = -INFINITY;
         }
     }
-    float mx = -INFINITY;
+    // Exponentials against the current reference m, without a row max:
+    // as long as no lane's sum over its 32 scores exceeds 2^8 (so no single
+    // probability does), they are kept. Otherwise (a row max that grew, an
+    // overflow) and while a row has no reference yet, the reference moves to
+    // the row max, O and l are rescaled, and the exponentials are taken
+    // again. Either way O and l stay relative to one reference, so the
+    // result is exact. (The no-reference case must not take the fast path:
+    // m * c then differs from m * scale * log2(e) when scale is 0.)
+    float p[2 * 16];
+    float ls;
+    auto exps = [&]() {
+      const float mc = m * c;
 #pragma unroll
-    for (int mt = 0; mt < S::NMT; ++mt)
+      for (int mt = 0; mt < S::NMT; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
-    mx = max_with_other_half(mx);
-    const float m_new = fmaxf(m, mx);
-    if (wave_any((m_new - m) * c > 8.f || m == -FLT_MAX)) {
+        for (int r = 0; r < 16; ++r)
+          // c > 0 always (the host passes max(scale*log2(e), FLT_MIN)), so a
+          // hidden score (-inf) gives exactly 0.
+          p[mt * 16 + r] = __builtin_amdgcn_exp2f(fmaf(s[mt][r], c, -mc));
+      float t[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) t[j] = p[2 * j] + p[2 * j + 1];
+#pragma unroll
+      for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+        for (int j = 0; j < w; ++j) t[j] = t[2 * j] + t[2 * j + 1];
+      ls = t[0];
+    };
+    exps();
+    if (wave_any(!(ls <= 256.f) || m == -FLT_MAX)) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < S::NMT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
+      mx = max_with_other_half(mx);
+      const float m_new = fmaxf(m, mx);
       const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
       m = m_new;
       l *= alpha;
@@ -594,28 +623,18 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a) {
       for (int dt = 0; dt < S::NDT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      exps();
     }
-    const float mc = m * c;
-    // Operand k = 2*mt + u packs scores s[mt][8u .. 8u+8) and is written to
-    // words [4k, 4k+4) of s, all of which were read by earlier operands.
-    // Each packed pair goes straight to its word: reading words back out of
-    // a vector assembled from packed 16-bit pairs mis-compiles.
+    l += ls;
+    // Operand k = 2*mt + u packs probabilities 8u .. 8u+8 of key block mt
+    // into words [4k, 4k+4) of s, all of which were read above. Each packed
+    // pair goes straight to its word: reading words back out of a vector
+    // assembled from packed 16-bit pairs mis-compiles.
 #pragma unroll
-    for (int mt = 0; mt < S::NMT; ++mt)
+    for (int k = 0; k < S::NPF; ++k)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        float p[KH];
-#pragma unroll
-        for (int jj = 0; jj < KH; ++jj) {
-          // c > 0 always (the host passes max(scale*log2(e), FLT_MIN)), so
-          // a hidden score (-inf) gives exactly 0.
-          p[jj] = __builtin_amdgcn_exp2f(fmaf(s[mt][u * KH + jj], c, -mc));
-        }
-        const int k = mt * 2 + u;
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-          s[k / 4][(k % 4) * 4 + w] = __builtin_bit_cast(float, E::pack2(p[2 * w], p[2 * w + 1], l));
-      }
+      for (int w = 0; w < 4; ++w)
+        s[k / 4][(k % 4) * 4 + w] = __builtin_bit_cast(float, E::pack_pair(p[8 * k + 2 * w], p[8 * k + 2 * w + 1]));
   };
 
   if (nkv == 0) {  // an empty slice: nothing to visit, an empty partial
