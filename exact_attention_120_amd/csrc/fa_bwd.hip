@@ -452,18 +452,13 @@ struct Bwd16Shape {
   static constexpr int OFF_LSE = 2 * TILE;           // LSE * log2(e), float32
   static constexpr int OFF_DSUM = 2 * TILE + kStepQ * 4;
   static constexpr int STAGE = 2 * TILE + 2 * kStepQ * 4;
-  static constexpr int DS_ROWB = kStepQ * 2;         // dS [key][query]
-  static constexpr int LDS = 2 * STAGE + kBN * DS_ROWB;
+  static constexpr int LDS = 2 * STAGE;
   static constexpr int UNITS = D / 8;                // 16-byte units per row
   static constexpr int NLD = kStepQ * UNITS / kThreads;
-  static constexpr int NKLD = kBN * UNITS / kThreads;
   static constexpr int NQK = D / 16;                 // MFMAs over the head dim
   static constexpr int NDT = D / 32;                 // 32-wide head-dim blocks
   static constexpr int NP = kStepQ / 16;             // P / dS operands per step
-  static constexpr int NKT = kBN / 16;               // K^T operands (dQ product)
-  static constexpr int DQ_UNITS = 2 * NDT / 4;       // (query block, head-dim block) per wave
-  static_assert(NLD * kThreads == kStepQ * UNITS && NKLD * kThreads == kBN * UNITS, "even split");
-  static_assert(kBN * ROWB <= 2 * STAGE, "the K tile is staged in the stage buffers");
+  static_assert(NLD * kThreads == kStepQ * UNITS, "even split");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -475,7 +470,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd16_kernel(BwdArgs a) {
   constexpr int ROWB = S::ROWB;
 
   __shared__ __attribute__((aligned(16))) char lds[S::LDS];
-  char* const dsl = lds + 2 * S::STAGE;
 
   const int N = a.N;
   const int nkt = (N + kBN - 1) / kBN;
@@ -510,25 +504,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd16_kernel(BwdArgs a) {
     pin_acc(kb[i]);
     pin_acc(vb[i]);
   }
-
-  // The workgroup's K tile (swizzled) through the stage buffers, then each
-  // wave keeps, as B operands of dQ = dS K, K^T for the head-dim block it
-  // reduces dQ over (natural key order).
-#pragma unroll
-  for (int j = 0; j < S::NKLD; ++j) {
-    const int idx = tid + kThreads * j, row = idx / S::UNITS, u = idx % S::UNITS;
-    st<u32x4>(lds + tile_off<ROWB>(row, u * 16), K.ld16(((k0 + row) * D + u * 8) * 2));
-  }
-  __syncthreads();
-  const int dblk = wave % S::NDT;
-  const int qb0 = wave / S::NDT;  // first query block of this wave's dQ units
-  Raw kq[S::NKT];
-#pragma unroll
-  for (int t = 0; t < S::NKT; ++t) {
-    kq[t] = tr_operand<ROWB, true>(lds, 16 * t, 32 * dblk, lane);
-    pin_acc(kq[t]);
-  }
-  __syncthreads();
 
   // Per-lane byte offsets of the 16-byte A-operand reads of S and dP: row
   // `col` (plus 32 per query block), unit h*D/16 + i.
@@ -584,17 +559,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd16_kernel(BwdArgs a) {
     if (tid < 2 * kStepQ) st<float>(stage + S::OFF_LSE + tid * 4, stat);
   };
 
-  // Step j covers query head g = j / ns, query step it0 + (j % ns + shift)
-  // mod ns. Each head's steps are visited starting at a per-workgroup
-  // offset, so that the workgroups of a head (which run concurrently on one
-  // XCD) add into different dQ rows at any moment instead of all contending
-  // for the same cache lines.
-  const int shift = (int)((long long)(k0 / kBN) * ns / nkt);
+  // Step j covers query head g = j / ns, query step it0 + j % ns.
   const int nsteps = grp * ns;
   auto step_at = [&](int j, int& g, int& q0) {
     g = j / ns;
-    const int t = j - g * ns + shift;
-    q0 = (it0 + (t >= ns ? t - ns : t)) * kStepQ;
+    q0 = (it0 + j - g * ns) * kStepQ;
   };
   int g_next, q_next;
   step_at(0, g_next, q_next);
@@ -612,9 +581,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd16_kernel(BwdArgs a) {
 
     // Per 32-query block: S = Q K^T and dP = dO V^T (lane = key, registers
     // = queries); P = exp2(S*scale*log2e - LSE*log2e) and dS = P * (dP - D),
-    // packed as B operands (P^T, dS^T over the step's queries); dS also goes
-    // to LDS. Operand p = 2*qb + u covers registers [8u, 8u+8) of block qb,
-    // i.e. queries 16p + 4h + 0..3 and 16p + 8 + 4h + 0..3.
+    // packed as B operands (P^T, dS^T over the step's queries). Operand
+    // p = 2*qb + u covers registers [8u, 8u+8) of block qb, i.e. queries
+    // 16p + 4h + 0..3 and 16p + 8 + 4h + 0..3.
     const bool need_mask =
         !block_all_visible(q0, q0 + kStepQ - 1, kw0, kw0 + 31, N, CAUSAL, a.wl, a.wr);
     Raw pf[S::NP], sf[S::NP];
@@ -653,7 +622,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd16_kernel(BwdArgs a) {
           pw[2 * k + 1] = E::pack2(pe[2], pe[3], unused);
           sw[2 * k] = E::pack2(de[0], de[1], unused);
           sw[2 * k + 1] = E::pack2(de[2], de[3], unused);
-          st<u32x2>(dsl + tile_off<S::DS_ROWB>(wave * 32 + col, ql * 2), u32x2{sw[2 * k], sw[2 * k + 1]});
         }
         pf[2 * qb + u] = Raw{pw[0], pw[1], pw[2], pw[3]};
         sf[2 * qb + u] = Raw{sw[0], sw[1], sw[2], sw[3]};
@@ -669,30 +637,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd16_kernel(BwdArgs a) {
         dkt[dt] = E::mma(tr_operand<ROWB, false>(stage, 16 * p, 32 * dt, lane), sf[p], dkt[dt]);
       }
     }
-    __syncthreads();  // dS of all four waves is in LDS
-
-    // dQ[q, d] += sum over the 128 keys of dS[q, key] K[key, d] (unscaled):
-    // C = dQ block (lane = head-dim column, registers = query rows).
-#pragma unroll
-    for (int n = 0; n < S::DQ_UNITS; ++n) {
-      const int qb = qb0 + n * (4 / S::NDT);
-      f32x16 acc = f32x16{};
-#pragma unroll
-      for (int t = 0; t < S::NKT; ++t)
-        acc = E::mma(tr_operand<S::DS_ROWB, true>(dsl, 16 * t, 32 * qb, lane), kq[t], acc);
-      float* dst = a.dq_acc + ((size_t)(bq0 + g) * N + q0 + 32 * qb + 4 * half) * D + dblk * 32 + col;
-      if (q0 + kStepQ <= N) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          unsafeAtomicAdd(dst + (8 * (r >> 2) + (r & 3)) * D, acc[r]);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (q0 + 32 * qb + 8 * (r >> 2) + 4 * half + (r & 3) < N)
-            unsafeAtomicAdd(dst + (8 * (r >> 2) + (r & 3)) * D, acc[r]);
-      }
-    }
-
     if (j + 1 < nsteps) store(lds + ((j + 1) & 1) * S::STAGE);
     __syncthreads();
   }
@@ -717,6 +661,283 @@ __global__ __launch_bounds__(kThreads, 1) void bwd16_kernel(BwdArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// 16-bit dQ kernel: query tiles outer, key tiles inner (the forward's
+// decomposition), so dQ accumulates in registers and is written once, with
+// no atomics. Per 32-key tile it recomputes S^T = K Q^T and dP^T = V dO^T,
+// forms dS = P * (dP - D) with P = exp2(S*scale*log2e - LSE*log2e), and
+// adds dQ^T += K^T dS^T (K^T read transposed from the same K tile).
+//
+// A workgroup has 8 waves covering 256 query rows of one head. As in the
+// forward kernel, the waves form two groups of four (one wave of each group
+// per SIMD) and alternate a matrix phase (MFMAs) and a vector phase (dS),
+// one barrier per phase, group B one phase behind group A. K and V tiles of
+// 32 keys use the swizzled row layout of the key-outer kernel (conflict-free
+// for both 16-byte row reads and transposing reads). K tile i is read in the
+// matrix phases of steps i (S) and i + 1 (dQ), so K has three buffers, V two.
+// Group A streams K (tile i + 1 loaded in its matrix phase i, stored in its
+// vector phase i); group B streams V (tile i + 2 loaded in its matrix phase
+// i, stored in its vector phase i, which comes before the matrix phase i + 1
+// of group A).
+
+constexpr int kDQThreads = 512;
+constexpr int kDQGroup = 256;  // threads per wave group
+constexpr int kDQBM = 256;     // query rows per workgroup
+constexpr int kDQBN = 32;      // keys per tile
+
+template <int D>
+struct DQShape {
+  static constexpr int ROWB = D * 2;
+  static constexpr int TILE = kDQBN * ROWB;
+  static constexpr int NKBUF = 3, NVBUF = 2;
+  static constexpr int LDS = (NKBUF + NVBUF) * TILE;
+  static constexpr int NQK = D / 16;                     // MFMAs over the head dim
+  static constexpr int NDT = D / 32;                     // head-dim blocks of dQ
+  static constexpr int UNITS = D / 8;                    // 16-byte units per row
+  static constexpr int NLD = kDQBN * UNITS / kDQGroup;   // loads per thread per tile
+  static_assert(NLD * kDQGroup == kDQBN * UNITS, "even split");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(kDQThreads, 1) void bwd_dq16_kernel(BwdArgs a) {
+  using S = DQShape<D>;
+  using E = Elem<T>;
+  using Raw = u32x4;
+  constexpr int ROWB = S::ROWB;
+
+  __shared__ __attribute__((aligned(16))) char lds[S::LDS];
+  char* const kbuf = lds;
+  char* const vbuf = lds + S::NKBUF * S::TILE;
+
+  const int N = a.N;
+  const int nqt = (N + kDQBM - 1) / kDQBM;
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = lin / nqt;
+  const int qtile = CAUSAL ? nqt - 1 - lin % nqt : lin % nqt;
+  const int q0 = qtile * kDQBM;
+
+  const size_t qhead = (size_t)bh * N;
+  // Query head h reads K/V head h / (H / Hkv).
+  const size_t kvhead = (size_t)((bh / a.H) * a.Hkv + (bh % a.H) / (a.H / a.Hkv)) * N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const HeadBuf Q(reinterpret_cast<const T*>(a.q) + qhead * D, head_bytes);
+  const HeadBuf G(reinterpret_cast<const T*>(a.dout) + qhead * D, head_bytes);
+  const HeadBuf K(reinterpret_cast<const T*>(a.k) + kvhead, head_bytes);
+  const HeadBuf V(reinterpret_cast<const T*>(a.v) + kvhead, head_bytes);
+  T* dQ = reinterpret_cast<T*>(a.dq) + qhead * D;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int group = wave >> 2;  // 0: A, 1: B (one phase behind)
+  const int gtid = tid & (kDQGroup - 1);
+  const int col = lane & 31, half = lane >> 5;
+  const int qw0 = q0 + wave * 32;  // first query row of this wave
+  const int qrow = qw0 + col;      // the query row this lane serves
+
+  // Key tiles t0 .. t0+nkv-1 hold a key some of the workgroup's rows see;
+  // this wave's rows see tiles [w_lo, w_end) of them (none if past N).
+  const int qlast = min(q0 + kDQBM, N) - 1;
+  const int t0 = first_visible_key(q0, a.wl) / kDQBN;
+  const int nkv = last_visible_key(qlast, N, CAUSAL, a.wr) / kDQBN - t0 + 1;
+  int w_lo = nkv + 1, w_end = -1;
+  if (qw0 < N) {
+    w_lo = first_visible_key(qw0, a.wl) / kDQBN - t0;
+    w_end = last_visible_key(min(qw0 + 31, N - 1), N, CAUSAL, a.wr) / kDQBN - t0 + 1;
+  }
+
+  // This row's LSE (log2 units) and D; rows past N get LSE = +inf, so their
+  // probabilities (and dS) are exactly 0.
+  const float lr = qrow < N ? a.lse[qhead + qrow] * kLog2e : INFINITY;
+  const float dr = qrow < N ? a.dsum[qhead + qrow] : 0.f;
+
+  // Q^T and dO^T as MFMA B operands: lane half h holds head-dim elements
+  // [h*D/2, h*D/2 + D/2) of its row, 8 per MFMA.
+  Raw qf[S::NQK], gf[S::NQK];
+#pragma unroll
+  for (int i = 0; i < S::NQK; ++i) {
+    const int off = (qrow * D + half * (D / 2) + i * 8) * 2;
+    qf[i] = Q.ld16(off);
+    gf[i] = G.ld16(off);
+  }
+  // This lane's 16-byte A-operand reads of a K or V tile: row `col` (+32
+  // for the second key block), elements half*D/2 + 8i, i.e. 16-byte unit
+  // half*D/16 + i of the row, XOR-swizzled by the row (mod 16, so the same
+  // for both key blocks).
+  const int arow = col * ROWB;
+  const int aswz = row_swz<ROWB>(col);
+  auto aoff = [&](int i) { return arow + (((half * (D / 16) + i) ^ aswz) << 4); };
+
+  const float c = a.scale_log2;
+  f32x16 dq[S::NDT];
+#pragma unroll
+  for (int dt = 0; dt < S::NDT; ++dt) dq[dt] = f32x16{};
+  // Scores of the current tile, then its dS packed as the two dS^T B
+  // operands into words 0-7 of s (operand k in words [4k, 4k+4)); dP
+  // alongside.
+  f32x16 s = f32x16{}, dp = f32x16{};
+
+  // Matrix phase: dQ^T += K^T dS^T for the previous tile (DQ, from the
+  // packed words of s), then S^T = K Q^T and dP^T = V dO^T for the current
+  // one (SP). The MFMAs run in chunks of four; the LDS operands of chunk
+  // c + 1 are read while chunk c computes. DQ chunk cc covers head-dim
+  // blocks 2cc and 2cc + 1 (two operands each); SP chunk j covers product
+  // j / QKH (0: S from K, 1: dP from V) and head-dim operands 4h .. 4h + 3
+  // with h = j % QKH.
+  auto mphase = [&](const char* kprev, const char* kcur, const char* vcur, auto dq_c, auto sp_c) {
+    constexpr bool DQ = decltype(dq_c)::value, SP = decltype(sp_c)::value;
+    constexpr int QKH = S::NQK / 4;  // chunks per product
+    constexpr int NDQC = DQ ? S::NDT / 2 : 0;
+    constexpr int NC = NDQC + (SP ? 2 * QKH : 0);
+    const f32x16 x = s;
+    const Raw dsf[2] = {__builtin_bit_cast(Raw, __builtin_shufflevector(x, x, 0, 1, 2, 3)),
+                        __builtin_bit_cast(Raw, __builtin_shufflevector(x, x, 4, 5, 6, 7))};
+    Raw op[2][4];
+    auto fetch = [&](int cc, Raw(&dst)[4]) {
+      if (cc < NDQC) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) dst[u] = tr_operand<ROWB, false>(kprev, 16 * (u & 1), 32 * (2 * cc + (u >> 1)), lane);
+      } else {
+        const int j = cc - NDQC, pr = j / QKH, h = j % QKH;
+        const char* tp = pr == 0 ? kcur : vcur;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) dst[u] = ld<Raw>(tp + aoff(4 * h + u));
+      }
+    };
+    auto compute = [&](int cc, const Raw(&src)[4]) {
+      if (cc < NDQC) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) dq[2 * cc + (u >> 1)] = E::mma(src[u], dsf[u & 1], dq[2 * cc + (u >> 1)]);
+      } else {
+        const int j = cc - NDQC, pr = j / QKH, h = j % QKH;
+        f32x16& acc = pr == 0 ? s : dp;
+        if (h == 0) acc = f32x16{};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc = E::mma(src[u], pr == 0 ? qf[4 * h + u] : gf[4 * h + u], acc);
+      }
+    };
+    __builtin_amdgcn_s_setprio(1);
+    fetch(0, op[0]);
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      if (cc + 1 < NC) fetch(cc + 1, op[(cc + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(cc, op[cc & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // Vector phase: dS = P * (dP - D) for the current tile, packed into s
+  // (word w of operand u pairs registers 8u + 2w, 8u + 2w + 1; every word is
+  // written after the scores it overwrites were read). Hidden keys get
+  // S = -inf, so P = 0 and dS = 0.
+  auto vphase = [&](int k0) {
+    if (!block_all_visible(qw0, qw0 + 31, k0, k0 + kDQBN - 1, N, CAUSAL, a.wl, a.wr)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (!key_visible(key, qrow, N, CAUSAL, a.wl, a.wr)) s[r] = -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float d[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[8 * u + e], c, -lr));
+        d[e] = p * (dp[8 * u + e] - dr);
+      }
+#pragma unroll
+      for (int w = 0; w < 4; ++w) s[4 * u + w] = __builtin_bit_cast(float, E::pack_pair(d[2 * w], d[2 * w + 1]));
+    }
+  };
+
+  // Global -> LDS staging of one group's tile (rows past N read as zeros).
+  u32x4 stg[S::NLD];
+  auto gload = [&](const HeadBuf& X, int tile) {
+#pragma unroll
+    for (int j = 0; j < S::NLD; ++j) {
+      const int idx = gtid + kDQGroup * j, row = idx / S::UNITS, u = idx % S::UNITS;
+      stg[j] = X.ld16(((t0 + tile) * kDQBN * D + row * D + u * 8) * 2);
+    }
+  };
+  auto lstore = [&](char* tile) {
+#pragma unroll
+    for (int j = 0; j < S::NLD; ++j) {
+      const int idx = gtid + kDQGroup * j, row = idx / S::UNITS, u = idx % S::UNITS;
+      st<u32x4>(tile + tile_off<ROWB>(row, u * 16), stg[j]);
+    }
+  };
+  auto kt = [&](int i) -> char* { return kbuf + (i % S::NKBUF) * S::TILE; };
+  auto vt = [&](int i) -> char* { return vbuf + (i % S::NVBUF) * S::TILE; };
+
+  // Prologue: K tile 0 (group A), V tiles 0 and 1 (group B).
+  const bool kgrp = group == 0;  // group A streams K, group B V
+  gload(kgrp ? K : V, 0);
+  lstore(kgrp ? kt(0) : vt(0));
+  if (!kgrp && nkv > 1) {
+    gload(V, 1);
+    lstore(vt(1));
+  }
+#pragma unroll
+  for (int i = 0; i < S::NQK; ++i) {
+    settle(qf[i]);
+    settle(gf[i]);
+  }
+  __syncthreads();
+
+  // Step i is a matrix phase M(i) (dQ of tile i-1; S and dP of tile i) then
+  // a vector phase V(i) (dS of tile i), each ending at a barrier; group B
+  // runs one phase behind group A (one extra barrier first, A one extra at
+  // the end). Group A loads K tile i + 1 in M(i) and stores it in V(i);
+  // group B loads V tile i + 2 in M(i) and stores it in V(i). K tile j lives
+  // in buffer j % 3, V tile j in buffer j % 2; each store lands in a buffer
+  // whose last readers passed an earlier barrier. At step w_lo (> 0) the dQ
+  // half adds the zero initial dS; at step w_end (< nkv) the S, dP half is
+  // unused.
+  const HeadBuf& X = kgrp ? K : V;
+  if (!kgrp) __syncthreads();
+  {
+    const int lt = kgrp ? 1 : 2;
+    if (lt < nkv) gload(X, lt);
+    if (w_lo == 0 && w_end > 0) mphase(kt(0), kt(0), vt(0), BoolC<false>{}, BoolC<true>{});
+    __syncthreads();
+    if (w_lo == 0 && w_end > 0) vphase(t0 * kDQBN);
+    if (lt < nkv) lstore(kgrp ? kt(lt) : vt(lt));
+    __syncthreads();
+  }
+  for (int i = 1; i < nkv; ++i) {
+    const int lt = kgrp ? i + 1 : i + 2;
+    if (lt < nkv) gload(X, lt);
+    if (w_lo <= i && i <= w_end) mphase(kt(i - 1), kt(i), vt(i), BoolC<true>{}, BoolC<true>{});
+    __syncthreads();
+    if (w_lo <= i && i < w_end) vphase((t0 + i) * kDQBN);
+    if (lt < nkv) lstore(kgrp ? kt(lt) : vt(lt));
+    __syncthreads();
+  }
+  // Final matrix phase: dQ of the last tile.
+  if (w_end == nkv) mphase(kt(nkv - 1), kt(nkv - 1), vt(0), BoolC<true>{}, BoolC<false>{});
+  __syncthreads();
+  if (kgrp) __syncthreads();
+
+  // Epilogue: dQ = scale * accumulator; lane = query row, registers =
+  // head-dim rows of dQ^T.
+  if (w_end <= 0 || qrow >= N) return;
+  T* qrow_p = dQ + (size_t)qrow * D;
+  const float sc = a.scale;
+#pragma unroll
+  for (int dt = 0; dt < S::NDT; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = dt * 32 + 8 * g + 4 * half;
+      const f32x16& v = dq[dt];
+      st<u32x2>(qrow_p + d0, u32x2{E::bits(v[4 * g] * sc) | ((uint32_t)E::bits(v[4 * g + 1] * sc) << 16),
+                                   E::bits(v[4 * g + 2] * sc) | ((uint32_t)E::bits(v[4 * g + 3] * sc) << 16)});
+    }
+}
+
 // D_i = sum_k dO_ik O_ik (float32) and dQ accumulator rows cleared.
 // TPR threads per row, 16 bytes of O and dO each.
 template <typename T, int D>
@@ -736,9 +957,11 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
     const T* gp = reinterpret_cast<const T*>(&g);
 #pragma unroll
     for (int e = 0; e < EPV; ++e) acc = fmaf((float)op[e], (float)gp[e], acc);
-    float* z = a.dq_acc + off;
+    if constexpr (sizeof(T) == 4) {  // 16-bit types write dQ without an accumulator
+      float* z = a.dq_acc + off;
 #pragma unroll
-    for (int e = 0; e < EPV; e += 4) st<f32x4>(z + e, f32x4{0.f, 0.f, 0.f, 0.f});
+      for (int e = 0; e < EPV; e += 4) st<f32x4>(z + e, f32x4{0.f, 0.f, 0.f, 0.f});
+    }
   }
 #pragma unroll
   for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
@@ -787,7 +1010,14 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
     hipError_t e = hipLaunchKernel(fn, grid, dim3(kThreads), kargs, 0, stream);
     if (e != hipSuccess) return e;
   }
-  {
+  if constexpr (sizeof(T) == 2) {
+    void* kargs[] = {&args};
+    const int nqt = (a.N + kDQBM - 1) / kDQBM;
+    const dim3 grid((unsigned)((long long)a.B * a.H * nqt));
+    const void* fn = a.causal ? reinterpret_cast<const void*>(&bwd_dq16_kernel<T, D, true>)
+                              : reinterpret_cast<const void*>(&bwd_dq16_kernel<T, D, false>);
+    return hipLaunchKernel(fn, grid, dim3(kDQThreads), kargs, 0, stream);
+  } else {
     long long n4 = rows * D / 4;
     void* kargs[] = {&args, &n4};
     const dim3 grid((unsigned)((n4 + kThreads - 1) / kThreads));
