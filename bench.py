@@ -9,12 +9,13 @@ FLOP convention: forward 4*B*H*N^2*d (halved when causal); backward 2.5x
 the forward. value = (fwd + bwd FLOP) / step time, in TFLOP/s.
 
 Roofline: every fa_fwd and fa_bwd call in the timed region is bracketed by
-HIP events on the stream it runs on. fa_fwd is one kernel; fa_bwd is three,
-of which the main kernel holds all the matrix work (the row-term and dQ
-conversion kernels are memory-bound and take well under 1% of the call, per
-the committed rocprofv3 trace). `roofline` describes the direction that
-takes longer (the dominant kernel); `roofline_fwd` / `roofline_bwd` give
-both. achieved = algorithmic FLOP per call / mean call duration, against the
+HIP events on the stream it runs on. fa_fwd is one kernel. fa_bwd (16-bit
+types) is three kernels back to back on that stream: the row term D
+(memory-bound, well under 1% of the call), the key-outer dK/dV kernel and
+the query-outer dQ kernel, which together hold all the matrix work; the
+committed rocprofv3 trace gives their split. `roofline` describes the
+direction that takes longer; `roofline_fwd` / `roofline_bwd` give both.
+achieved = algorithmic FLOP per call / mean call duration, against the
 MI355X dense bf16/fp16 MFMA peak (2.5 PFLOP/s; fp32 MFMA: 157.3 TFLOP/s).
 `traffic` (measured HBM bytes per call: FETCH_SIZE and WRITE_SIZE scaled by
 what the same counters read for a plain copy of known size) is read from the
@@ -28,6 +29,8 @@ reported in the same unit.
 Other modes (used to collect the rocprofv3 summaries under profiles/):
   --only fwd|bwd        time only that direction (no CPU baseline)
   --sweep               forward over N in {1k,2k,4k,8k,16k}, B=1 H=16 d=128
+  --variants            split-KV, grouped K/V heads and a local window against
+                        the plain calls (one JSON line per case)
   --copy-bytes BYTES    a plain device copy of BYTES bytes (counter scaling)
   --summarize DIR       turn rocprofv3 output under DIR into a text table
 """
@@ -192,8 +195,8 @@ def run_main(args):
     j, roofs = 0, {}
     for name, on, fl, kern in (
             ("fwd", do_fwd, fwd_flop, "fwd_pp_kernel (the one kernel of fa_fwd)"),
-            ("bwd", do_bwd, bwd_flop, "fa_bwd: bwd16_kernel (all MFMA work) + bwd_pre_kernel"
-                                      " + bwd_dq_kernel (memory-bound, <1% of the call)")):
+            ("bwd", do_bwd, bwd_flop, "fa_bwd call: bwd_pre_kernel (D, <1%) + bwd16_kernel"
+                                      " (dK, dV) + bwd_dq16_kernel (dQ)")):
         if not on:
             continue
         ms = sum(per[j]) / len(per[j])
@@ -229,6 +232,82 @@ def run_sweep(args):
             print(json.dumps({"sweep_N": n, "causal": causal}), flush=True)
 
 
+def run_variants(args):
+    """Time the variant rows against the plain calls (HIP events on the
+    current stream, back-to-back calls with preallocated buffers): split-KV
+    on short/few-head shapes, grouped K/V heads and a local window at
+    N = 16384. One JSON line per case."""
+    import torch
+
+    import exact_attention_120_amd as fa
+    from fa_inputs import make_inputs
+
+    dev = torch.device("cuda:0")
+
+    def per_call_ms(fn, min_s=0.4):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        n, t0 = 1, time.time()
+        while True:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(n):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            if ms * 1e-3 >= min_s or time.time() - t0 > 5 * min_s:
+                return ms / n
+            n *= 2
+
+    # Split-KV: the library's slice count and fixed counts against fa_fwd.
+    for (B, H, N, d, causal) in ((2, 8, 1024, 64, True), (1, 8, 2048, 128, False),
+                                 (1, 4, 4096, 128, True)):
+        inp = make_inputs(B, H, N, d, "bf16", seed=0)
+        q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+        o, lse = torch.empty_like(q), torch.empty((B, H, N), device=dev)
+        sc = d ** -0.5
+        flop = 4.0 * B * H * N * N * d / (2 if causal else 1)
+        res = {"case": "splitkv", "B": B, "H": H, "N": N, "d": d, "causal": causal,
+               "auto_splits": fa.fa_fwd_num_splits(B, H, N, d, q.dtype)}
+        res["plain_us"] = per_call_ms(lambda: fa.fa_fwd(q, k, v, o, lse, sc, causal)) * 1e3
+        for ns in sorted({2, 4, 8, res["auto_splits"]}):
+            nb = fa.fa_fwd_splitkv_workspace_size(B, H, N, d, q.dtype, ns)
+            ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+            res[f"split{ns}_us"] = per_call_ms(
+                lambda: fa.fa_fwd_splitkv(q, k, v, o, lse, sc, causal, ns, ws)) * 1e3
+        best = min(v for kk, v in res.items() if kk.startswith("split"))
+        res["plain_tflops"] = flop / (res["plain_us"] * 1e-6) / 1e12
+        res["best_split_tflops"] = flop / (best * 1e-6) / 1e12
+        print(json.dumps(res), flush=True)
+
+    # Grouped K/V heads and a local window, forward and backward, bf16
+    # B=1 H=16 N=16384 d=128. FLOP counts only the visible (query, key) pairs.
+    B, H, N, d = 1, 16, 16384, 128
+    sc = d ** -0.5
+    for (hkv, causal, window) in ((16, False, None), (4, False, None), (1, False, None),
+                                  (16, True, None), (4, True, (1024, 0))):
+        inp = make_inputs(B, H, N, d, "bf16", seed=0, backward=True, kv_heads=hkv)
+        q, k, v, do = (inp[x].to(dev) for x in ("q", "k", "v", "do"))
+        o, lse = torch.empty_like(q), torch.empty((B, H, N), device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device=dev)
+        if window is None:
+            pairs = N * N / 2 if causal else N * N
+        else:
+            i = torch.arange(N, dtype=torch.float64)
+            pairs = float((torch.clamp(i, max=window[0]) + 1).sum())
+        fl = 4.0 * B * H * pairs * d
+        f_ms = per_call_ms(lambda: fa.fa_fwd_ex(q, k, v, o, lse, sc, causal, window))
+        b_ms = per_call_ms(lambda: fa.fa_bwd_ex(q, k, v, o, do, lse, dq, dk, dv, sc, causal, ws,
+                                                window))
+        print(json.dumps({"case": "heads_window", "B": B, "H": H, "Hkv": hkv, "N": N, "d": d,
+                          "causal": causal, "window": window, "fwd_ms": f_ms, "bwd_ms": b_ms,
+                          "fwd_tflops": fl / (f_ms * 1e-3) / 1e12,
+                          "bwd_tflops": 2.5 * fl / (b_ms * 1e-3) / 1e12}), flush=True)
+
+
 def run_copy(args):
     import torch
 
@@ -243,11 +322,13 @@ def run_copy(args):
 
 def _short(name: str) -> str:
     """Readable kernel name from a (possibly mangled) symbol."""
-    m = re.search(r"(fwd_pp_kernel|fwd_kernel|bwd16_kernel|bwd_main_kernel|bwd_pre_kernel|bwd_dq_kernel)"
-                  r"I([^E]*)", name)
+    m = re.search(r"(fwd_pp_kernel|fwd_kernel|fwd_merge_kernel|bwd16_kernel|bwd_main_kernel|"
+                  r"bwd_pre_kernel|bwd_dq16_kernel|bwd_dq_kernel)I(.*?)EEv", name)
     if m:
-        return m.group(1) + "<" + m.group(2).replace("DF16b", "bf16,").replace("DF16_", "f16,")\
-            .replace("Li", "d=").replace("Lb0", ",noncausal").replace("Lb1", ",causal") + ">"
+        args = m.group(2).replace("DF16b", "bf16,").replace("DF16_", "f16,").replace("f", "f32,", 1)\
+            if m.group(2).startswith("f") else m.group(2).replace("DF16b", "bf16,").replace("DF16_", "f16,")
+        args = args.replace("Li", "d=").replace("ELb0", ",noncausal").replace("ELb1", ",causal")
+        return m.group(1) + "<" + args.rstrip("E") + ">"
     return name[:70]
 
 
@@ -288,6 +369,7 @@ def main():
     p.add_argument("--only", choices=["fwd", "bwd"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--sweep", action="store_true")
+    p.add_argument("--variants", action="store_true")
     p.add_argument("--copy-bytes", type=int)
     p.add_argument("--summarize")
     args = p.parse_args()
@@ -302,6 +384,8 @@ def main():
         return run_copy(args)
     if args.sweep:
         return run_sweep(args)
+    if args.variants:
+        return run_variants(args)
     return run_main(args)
 
 
