@@ -10,18 +10,18 @@
 //   dP = dO V^T                         D_i = sum_k dO_ik O_ik
 //   dS = P * (dP - D)                   dK = scale * dS^T Q,  dQ = scale * dS K
 //
-// Three kernels on the caller's stream:
-//   1. bwd_pre:  D (float32, workspace) and a zeroed float32 dQ accumulator.
-//   2. bwd_main: one workgroup per 128-key tile of one head (4 waves x 32
-//      keys); the query tiles are the inner loop (causal: only tiles at or
-//      below the diagonal). Each wave keeps its K and V rows as MFMA
-//      operands and its dK^T, dV^T accumulators in registers for the whole
-//      loop. S = Q K^T and dP = dO V^T put one key per lane, so P and dS feed
-//      dV^T += dO^T P and dK^T += Q^T dS straight from registers (Q^T and
-//      dO^T are staged transposed in LDS next to Q and dO). dS goes through
-//      LDS once so the workgroup can form its whole 128-key contribution to
-//      dQ (dS K) and add it with one float32 atomic per element.
-//   3. bwd_dq:   dQ accumulator * scale -> dtype.
+// bf16/fp16: three kernels on the caller's stream, none with atomics:
+//   1. bwd_pre:   D (float32, workspace).
+//   2. bwd_kv16:  keys outer (128 per workgroup), query steps inner; dK and
+//      dV accumulate in registers. Each 32-key slice is shared by two waves
+//      of one SIMD, one forming P and dV, the other dP, dS and dK, in
+//      alternating matrix and vector phases.
+//   3. bwd_dq16:  queries outer (256 per workgroup), 32-key tiles inner (the
+//      forward's decomposition); S and dP are recomputed and dQ accumulates
+//      in registers, written once.
+// float32: bwd_pre (also zeroes a float32 dQ accumulator), bwd_main (keys
+// outer, dK/dV in registers, dQ added with one float32 atomic per element
+// per key tile), bwd_dq (accumulator * scale -> dQ).
 #include <float.h>
 
 #include "fa_device.hpp"
@@ -384,28 +384,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 16-bit (bf16, fp16) main kernel.
+// 16-bit (bf16, fp16) kernels: shared tile layout.
 //
-// Same decomposition as above (one workgroup = 4 waves x 32 keys, query
-// steps of 64 rows as the inner loop, dK^T and dV^T in registers, dQ through
-// float32 atomics), laid out for gfx950's LDS:
-//   * Q and dO tiles are stored once, row-major, with their 16-byte units
-//     XOR-swizzled by row (tile_off). The swizzle makes both access patterns
-//     free of bank conflicts: 16-byte row reads (the A operands of S = Q K^T
-//     and dP = dO V^T) and transposing 8-byte reads (ds_read_b64_tr_b16, the
-//     Q^T and dO^T operands of dK^T += Q^T dS and dV^T += dO^T P).
-//   * dS goes to LDS as [key][query] with 8-byte stores and comes back
-//     transposed (lane = query) as the A operand of dQ = dS K.
-//   * K^T operands for dQ are read once, transposed, from a swizzled K tile.
-//   * one wave per SIMD: K/V operands (64 registers), dK^T/dV^T (128) and
-//     K^T (32) stay in registers for the whole loop.
+// Q and dO (dK/dV kernel) and K and V (dQ kernel) tiles are stored
+// row-major with their 16-byte units XOR-swizzled by row (tile_off). The
+// swizzle makes both access patterns free of bank conflicts: 16-byte row
+// reads (A operands of the score products) and transposing 8-byte reads
+// (ds_read_b64_tr_b16, the transposed A operands of the gradient products).
 
-constexpr int kStepQ = 64;  // query rows per inner step
-
-// Keeps an MFMA source operand in the accumulation registers (AGPRs), which
-// MFMA instructions read directly: operands that only ever feed MFMAs then
-// leave the VGPR budget to the values the vector ALU works on.
-__device__ inline void pin_acc(u32x4& x) { asm volatile("" : "+a"(x)); }
+constexpr int kStepQ = 64;  // query rows per inner step of the dK/dV kernel
 
 // XOR swizzle of the 16-byte units of a tile row (ROWB bytes per row, 256 or
 // 128). Conflict-free for 16 lanes reading 16 bytes from 16 consecutive rows
@@ -444,27 +431,45 @@ __device__ inline u32x4 tr_operand(const char* tile, int row0, int col0, int lan
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
+// ---------------------------------------------------------------------------
+// 16-bit dK/dV kernel with 8 waves: keys outer (128 keys per workgroup),
+// query steps of 64 rows inner. Each 32-key slice of the workgroup's keys is
+// shared by the two waves of one SIMD, split by role:
+//   role A (waves 0-3): S = Q K^T, P = exp2(S*scale*log2e - LSE*log2e) and
+//                       dV^T += dO^T P; holds K and dV^T in registers;
+//   role B (waves 4-7): dP = dO V^T, dS = P * (dP - D) and dK^T += Q^T dS;
+//                       holds V and dK^T.
+// P goes from A to B through LDS (bf16, lane-private slots). Each wave runs
+// a matrix phase then a vector phase per step, each ending at a barrier,
+// with role B one phase behind role A, so that on every SIMD one role's
+// MFMAs overlap the other role's vector work (the ping-pong of the forward
+// kernel). Q/dO/LSE/D stages live in three LDS buffers.
+
+constexpr int kKVThreads = 512;
+
 template <int D>
-struct Bwd16Shape {
-  static constexpr int ROWB = D * 2;                 // Q / dO / K tile row bytes
-  static constexpr int TILE = kStepQ * ROWB;
+struct KVShape {
+  static constexpr int ROWB = D * 2;
+  static constexpr int TILE = kStepQ * ROWB;          // Q or dO of one step
   static constexpr int OFF_DO = TILE;
-  static constexpr int OFF_LSE = 2 * TILE;           // LSE * log2(e), float32
+  static constexpr int OFF_LSE = 2 * TILE;            // LSE * log2(e), float32
   static constexpr int OFF_DSUM = 2 * TILE + kStepQ * 4;
   static constexpr int STAGE = 2 * TILE + 2 * kStepQ * 4;
-  static constexpr int LDS = 2 * STAGE;
-  static constexpr int UNITS = D / 8;                // 16-byte units per row
-  static constexpr int NLD = kStepQ * UNITS / kThreads;
-  static constexpr int NQK = D / 16;                 // MFMAs over the head dim
-  static constexpr int NDT = D / 32;                 // 32-wide head-dim blocks
-  static constexpr int NP = kStepQ / 16;             // P / dS operands per step
-  static_assert(NLD * kThreads == kStepQ * UNITS, "even split");
+  static constexpr int NSTAGE = 3;
+  static constexpr int OFF_PX = NSTAGE * STAGE;       // P exchange: 4 slices x 4 KB
+  static constexpr int LDS = OFF_PX + 4 * 4096;
+  static constexpr int UNITS = D / 8;
+  static constexpr int NLD = kStepQ * UNITS / 256;    // loads per thread (one tensor, one role)
+  static constexpr int NQK = D / 16;
+  static constexpr int NDT = D / 32;
+  static constexpr int NP = kStepQ / 16;              // P / dS operands per step
+  static_assert(NLD * 256 == kStepQ * UNITS, "even split");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void bwd16_kernel(BwdArgs a) {
-  using S = Bwd16Shape<D>;
+__global__ __launch_bounds__(kKVThreads, 1) void bwd_kv16_kernel(BwdArgs a) {
+  using S = KVShape<D>;
   using E = Elem<T>;
   using Raw = u32x4;
   constexpr int ROWB = S::ROWB;
@@ -483,181 +488,254 @@ __global__ __launch_bounds__(kThreads, 1) void bwd16_kernel(BwdArgs a) {
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const HeadBuf K(reinterpret_cast<const T*>(a.k) + kvhead, head_bytes);
   const HeadBuf V(reinterpret_cast<const T*>(a.v) + kvhead, head_bytes);
-  T* dK = reinterpret_cast<T*>(a.dk) + kvhead;
-  T* dV = reinterpret_cast<T*>(a.dv) + kvhead;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool roleA = wave < 4;
+  const int slice = wave & 3;       // the 32-key slice this wave serves
   const int col = lane & 31, half = lane >> 5;
-  const int kw0 = k0 + wave * 32;  // first key of this wave
-  const int key = kw0 + col;       // the key this lane serves in S and dP
+  const int kw0 = k0 + slice * 32;  // first key of the slice
+  const int key = kw0 + col;        // the key this lane serves in S and dP
 
-  // This wave's K and V rows as B operands over the head dim (rows past N
-  // read as zeros): lane half h holds elements [h*D/2 + 8i, +8) for MFMA i.
-  Raw kb[S::NQK], vb[S::NQK];
+  // K (role A) or V (role B) rows of the slice as B operands over the head
+  // dim (rows past N read as zeros): lane half h holds elements
+  // [h*D/2 + 8i, +8) for MFMA i.
+  Raw kvb[S::NQK];
+  {
+    const HeadBuf& X = roleA ? K : V;
 #pragma unroll
-  for (int i = 0; i < S::NQK; ++i) {
-    const int off = (key * D + half * (D / 2) + i * 8) * 2;
-    kb[i] = K.ld16(off);
-    vb[i] = V.ld16(off);
-    pin_acc(kb[i]);
-    pin_acc(vb[i]);
+    for (int i = 0; i < S::NQK; ++i) kvb[i] = X.ld16((key * D + half * (D / 2) + i * 8) * 2);
   }
-
-  // Per-lane byte offsets of the 16-byte A-operand reads of S and dP: row
+  // Byte offsets of the 16-byte A-operand reads of a Q or dO tile: row
   // `col` (plus 32 per query block), unit h*D/16 + i.
   int aoff[S::NQK];
 #pragma unroll
   for (int i = 0; i < S::NQK; ++i) aoff[i] = tile_off<ROWB>(col, (half * (D / 2) + 8 * i) * 2);
 
-  // Query steps [it0, it0 + ns) hold every row that sees a key of the tile.
+  // Query steps [it0, it0 + ns) hold every row that sees a key of the tile;
+  // step j covers query head j / ns, step it0 + j % ns.
   const int it0 = first_query_seeing(k0, CAUSAL, a.wr) / kStepQ;
   const int ns = last_query_seeing(min(k0 + kBN, N) - 1, N, a.wl) / kStepQ - it0 + 1;
+  const int nsteps = grp * ns;
+  auto step_q0 = [&](int j) { return (it0 + j % ns) * kStepQ; };
   const float c = a.scale_log2;
 
-  f32x16 dkt[S::NDT], dvt[S::NDT];
+  f32x16 acc[S::NDT];  // role A: dV^T, role B: dK^T (rows = head dim, lane = key)
 #pragma unroll
-  for (int dt = 0; dt < S::NDT; ++dt) {
-    dkt[dt] = f32x16{};
-    dvt[dt] = f32x16{};
-  }
+  for (int dt = 0; dt < S::NDT; ++dt) acc[dt] = f32x16{};
+  f32x16 sc[2];        // role A: S of the step's two 32-query blocks; role B: dP
+  sc[0] = sc[1] = f32x16{};
+  Raw pf[S::NP];       // role A: P^T operands; role B: dS^T operands
+#pragma unroll
+  for (int p = 0; p < S::NP; ++p) pf[p] = Raw{0u, 0u, 0u, 0u};
 
-  // Next step's Q and dO units and one LSE or D value, staged in registers.
-  u32x4 sq[S::NLD], sg[S::NLD];
+  // Stage staging, split by role: role A streams Q and LSE, role B dO and
+  // D (each 256 threads; rows past N read as zeros, LSE = +inf there so
+  // their probabilities are exactly 0).
+  const int rtid = tid & 255;
+  u32x4 sx[S::NLD];
   float stat = 0.f;
-  auto load = [&](int g, int q0) {
-    const size_t qh = (size_t)(bq0 + g) * N;  // query head of the step
-    const HeadBuf Q(reinterpret_cast<const T*>(a.q) + qh * D, head_bytes);
-    const HeadBuf G(reinterpret_cast<const T*>(a.dout) + qh * D, head_bytes);
-    const float* lse = a.lse + qh;
-    const float* dsum = a.dsum + qh;
+  auto load = [&](int j) {
+    const int q0 = step_q0(j);
+    const size_t qh = (size_t)(bq0 + j / ns) * N;  // query head of the step
+    const HeadBuf X(reinterpret_cast<const T*>(roleA ? a.q : a.dout) + qh * D, head_bytes);
 #pragma unroll
-    for (int j = 0; j < S::NLD; ++j) {
-      const int idx = tid + kThreads * j, row = idx / S::UNITS, u = idx % S::UNITS;
-      const int off = ((q0 + row) * D + u * 8) * 2;
-      sq[j] = Q.ld16(off);
-      sg[j] = G.ld16(off);
+    for (int i = 0; i < S::NLD; ++i) {
+      const int idx = rtid + 256 * i, row = idx / S::UNITS, u = idx % S::UNITS;
+      sx[i] = X.ld16(((q0 + row) * D + u * 8) * 2);
     }
-    // Threads [0, 64) fetch LSE, [64, 128) D. Rows past N get LSE = +inf
-    // so their probabilities are exactly 0.
-    if (tid < kStepQ) {
-      const int row = q0 + tid;
-      stat = row < N ? lse[row] * kLog2e : INFINITY;
-    } else if (tid < 2 * kStepQ) {
-      const int row = q0 + tid - kStepQ;
-      stat = row < N ? dsum[row] : 0.f;
+    if (rtid < kStepQ) {
+      const int row = q0 + rtid;
+      stat = roleA ? (row < N ? a.lse[qh + row] * kLog2e : INFINITY) : (row < N ? a.dsum[qh + row] : 0.f);
     }
   };
-  auto store = [&](char* stage) {
+  auto store = [&](int j) {
+    char* stage = lds + (j % S::NSTAGE) * S::STAGE + (roleA ? 0 : S::OFF_DO);
 #pragma unroll
-    for (int j = 0; j < S::NLD; ++j) {
-      const int idx = tid + kThreads * j, row = idx / S::UNITS, u = idx % S::UNITS;
-      st<u32x4>(stage + tile_off<ROWB>(row, u * 16), sq[j]);
-      st<u32x4>(stage + S::OFF_DO + tile_off<ROWB>(row, u * 16), sg[j]);
+    for (int i = 0; i < S::NLD; ++i) {
+      const int idx = rtid + 256 * i, row = idx / S::UNITS, u = idx % S::UNITS;
+      st<u32x4>(stage + tile_off<ROWB>(row, u * 16), sx[i]);
     }
-    if (tid < 2 * kStepQ) st<float>(stage + S::OFF_LSE + tid * 4, stat);
+    if (rtid < kStepQ)
+      st<float>(lds + (j % S::NSTAGE) * S::STAGE + (roleA ? S::OFF_LSE : S::OFF_DSUM) + rtid * 4, stat);
   };
+  auto stage_of = [&](int j) -> const char* { return lds + (j % S::NSTAGE) * S::STAGE; };
+  char* const px = lds + S::OFF_PX + slice * 4096 + lane * 16;  // this lane's P slots
 
-  // Step j covers query head g = j / ns, query step it0 + j % ns.
-  const int nsteps = grp * ns;
-  auto step_at = [&](int j, int& g, int& q0) {
-    g = j / ns;
-    q0 = (it0 + j - g * ns) * kStepQ;
-  };
-  int g_next, q_next;
-  step_at(0, g_next, q_next);
-  load(g_next, q_next);
-  store(lds);
-  __syncthreads();
-
-  for (int j = 0; j < nsteps; ++j) {
-    const char* stage = lds + (j & 1) * S::STAGE;
-    const int g = g_next, q0 = q_next;
-    if (j + 1 < nsteps) {
-      step_at(j + 1, g_next, q_next);
-      load(g_next, q_next);
+  // Matrix phase of either role: first dV^T += dO^T P (role A) or
+  // dK^T += Q^T dS (role B) for step ja, with the transposed A operands read
+  // from that step's tile; then S (role A, from Q) or dP (role B, from dO)
+  // for step js (lane = key, registers = query rows of block qb). The MFMAs
+  // run in chunks of four; the LDS operands of chunk c + 1 are read while
+  // chunk c computes. Chunk c < NDT is head-dim block c of the accumulation,
+  // chunk NDT + 2 qb + h is query block qb, head-dim operands 4h .. 4h + 3.
+  auto mphase = [&](int ja, int js, auto acc_c, auto sc_c) {
+    constexpr int QKH = S::NQK / 4;
+    constexpr int NC = S::NDT + 2 * QKH;
+    const char* ta = stage_of(ja) + (roleA ? S::OFF_DO : 0);
+    const char* ts = stage_of(js) + (roleA ? 0 : S::OFF_DO);
+    constexpr int c0 = decltype(acc_c)::value ? 0 : S::NDT;
+    constexpr int c1 = decltype(sc_c)::value ? NC : S::NDT;
+    Raw op[2][4];
+    auto fetch = [&](int cc, Raw(&dst)[4]) {
+      if (cc < S::NDT) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) dst[p] = tr_operand<ROWB, false>(ta, 16 * p, 32 * cc, lane);
+      } else {
+        const int qb = (cc - S::NDT) / QKH, h = (cc - S::NDT) % QKH;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) dst[u] = ld<Raw>(ts + aoff[4 * h + u] + 32 * qb * ROWB);
+      }
+    };
+    auto compute = [&](int cc, const Raw(&src)[4]) {
+      if (cc < S::NDT) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) acc[cc] = E::mma(src[p], pf[p], acc[cc]);
+      } else {
+        const int qb = (cc - S::NDT) / QKH, h = (cc - S::NDT) % QKH;
+        f32x16 x = h == 0 ? f32x16{} : sc[qb];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x = E::mma(src[u], kvb[4 * h + u], x);
+        sc[qb] = x;
+      }
+    };
+    static_assert(S::NP == 4 && S::NQK % 4 == 0, "chunks of four MFMAs");
+    __builtin_amdgcn_s_setprio(1);
+    fetch(c0, op[0]);
+#pragma unroll
+    for (int cc = c0; cc < c1; ++cc) {
+      if (cc + 1 < c1) fetch(cc + 1, op[(cc - c0 + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(cc, op[(cc - c0) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-
-    // Per 32-query block: S = Q K^T and dP = dO V^T (lane = key, registers
-    // = queries); P = exp2(S*scale*log2e - LSE*log2e) and dS = P * (dP - D),
-    // packed as B operands (P^T, dS^T over the step's queries). Operand
-    // p = 2*qb + u covers registers [8u, 8u+8) of block qb, i.e. queries
-    // 16p + 4h + 0..3 and 16p + 8 + 4h + 0..3.
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // Role A, step j: P from S (hidden scores -> probability 0), packed as
+  // P^T operands (operand p = 2*qb + u covers registers [8u, 8u+8) of block
+  // qb: queries 16p + 4h + 0..3 and 16p + 8 + 4h + 0..3), also stored to the
+  // lane's slots for role B.
+  auto probabilities = [&](int j) {
+    const char* stage = stage_of(j);
+    const int q0 = step_q0(j);
     const bool need_mask =
         !block_all_visible(q0, q0 + kStepQ - 1, kw0, kw0 + 31, N, CAUSAL, a.wl, a.wr);
-    Raw pf[S::NP], sf[S::NP];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int i = 0; i < S::NQK; ++i) {
-        s = E::mma(ld<Raw>(stage + aoff[i] + 32 * qb * ROWB), kb[i], s);
-        dp = E::mma(ld<Raw>(stage + S::OFF_DO + aoff[i] + 32 * qb * ROWB), vb[i], dp);
-      }
-      if (need_mask) {  // hidden scores -> -inf (probability exactly 0)
+      if (need_mask) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qrow = q0 + 32 * qb + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (!key_visible(key, qrow, N, CAUSAL, a.wl, a.wr)) s[r] = -INFINITY;
+          if (!key_visible(key, qrow, N, CAUSAL, a.wl, a.wr)) sc[qb][r] = -INFINITY;
         }
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        uint32_t pw[4], sw[4];
+        uint32_t w[4];
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           const int ql = 32 * qb + 16 * u + 8 * k + 4 * half;  // first of 4 query rows
           const f32x4 l2 = ld<f32x4>(stage + S::OFF_LSE + ql * 4);
+          float pe[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pe[e] = __builtin_amdgcn_exp2f(fmaf(sc[qb][8 * u + 4 * k + e], c, -l2[e]));
+          w[2 * k] = E::pack_pair(pe[0], pe[1]);
+          w[2 * k + 1] = E::pack_pair(pe[2], pe[3]);
+        }
+        pf[2 * qb + u] = Raw{w[0], w[1], w[2], w[3]};
+        st<Raw>(px + (2 * qb + u) * 1024, pf[2 * qb + u]);
+      }
+    }
+  };
+  // Role B, step j: dS = P * (dP - D) with P read back from role A's slots,
+  // packed as dS^T operands (the same operand layout).
+  auto score_grads = [&](int j) {
+    const char* stage = stage_of(j);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const Raw pw = ld<Raw>(px + (2 * qb + u) * 1024);
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int ql = 32 * qb + 16 * u + 8 * k + 4 * half;
           const f32x4 dd = ld<f32x4>(stage + S::OFF_DSUM + ql * 4);
           float pe[4], de[4];
+          E::unpack_pair(pw[2 * k], pe[0], pe[1]);
+          E::unpack_pair(pw[2 * k + 1], pe[2], pe[3]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 8 * u + 4 * k + e;
-            pe[e] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -l2[e]));
-            de[e] = pe[e] * (dp[r] - dd[e]);
-          }
-          float unused = 0.f;
-          pw[2 * k] = E::pack2(pe[0], pe[1], unused);
-          pw[2 * k + 1] = E::pack2(pe[2], pe[3], unused);
-          sw[2 * k] = E::pack2(de[0], de[1], unused);
-          sw[2 * k + 1] = E::pack2(de[2], de[3], unused);
+          for (int e = 0; e < 4; ++e) de[e] = pe[e] * (sc[qb][8 * u + 4 * k + e] - dd[e]);
+          w[2 * k] = E::pack_pair(de[0], de[1]);
+          w[2 * k + 1] = E::pack_pair(de[2], de[3]);
         }
-        pf[2 * qb + u] = Raw{pw[0], pw[1], pw[2], pw[3]};
-        sf[2 * qb + u] = Raw{sw[0], sw[1], sw[2], sw[3]};
+        pf[2 * qb + u] = Raw{w[0], w[1], w[2], w[3]};
       }
-    }
+  };
 
-    // dV^T += dO^T P and dK^T += Q^T dS (A operands read transposed).
+  // Prologue: stages 0 and 1 in LDS.
+  load(0);
+  store(0);
+  if (nsteps > 1) {
+    load(1);
+    store(1);
+  }
 #pragma unroll
-    for (int dt = 0; dt < S::NDT; ++dt) {
-#pragma unroll
-      for (int p = 0; p < S::NP; ++p) {
-        dvt[dt] = E::mma(tr_operand<ROWB, false>(stage + S::OFF_DO, 16 * p, 32 * dt, lane), pf[p], dvt[dt]);
-        dkt[dt] = E::mma(tr_operand<ROWB, false>(stage, 16 * p, 32 * dt, lane), sf[p], dkt[dt]);
-      }
-    }
-    if (j + 1 < nsteps) store(lds + ((j + 1) & 1) * S::STAGE);
+  for (int i = 0; i < S::NQK; ++i) settle(kvb[i]);
+  __syncthreads();
+
+  // Step j of a wave is its matrix phase M(j) then its vector phase V(j),
+  // each ending at a barrier; role B runs one phase behind role A (one extra
+  // barrier first, A one extra at the end), so one role's MFMAs overlap the
+  // other's vector work:
+  //   A: M(j) = dV of step j-1, S of step j;   V(j) = P of step j (to LDS);
+  //   B: M(j) = dK of step j-1, dP of step j;  V(j) = dS of step j (P from LDS).
+  // Stage j is read from A's M(j) to B's M(j+1). Role A loads Q/LSE of stage
+  // j+1 in M(j) and stores them in V(j); role B loads dO/D of stage j+2 in
+  // M(j) and stores them in V(j). Stage j lives in buffer j % 3; each store
+  // lands in a buffer whose last readers passed an earlier barrier.
+  const int ahead = roleA ? 1 : 2;
+  auto vphase = [&](int j) {
+    if (roleA)
+      probabilities(j);
+    else
+      score_grads(j);
+  };
+  if (!roleA) __syncthreads();
+  {
+    if (roleA ? false : 2 < nsteps) load(2);
+    mphase(0, 0, BoolC<false>{}, BoolC<true>{});
+    __syncthreads();
+    vphase(0);
+    if (!roleA && 2 < nsteps) store(2);
     __syncthreads();
   }
+  for (int j = 1; j < nsteps; ++j) {
+    const int ls = j + ahead;
+    if (ls < nsteps) load(ls);
+    mphase(j - 1, j, BoolC<true>{}, BoolC<true>{});
+    __syncthreads();
+    vphase(j);
+    if (ls < nsteps) store(ls);
+    __syncthreads();
+  }
+  mphase(nsteps - 1, 0, BoolC<true>{}, BoolC<false>{});
+  __syncthreads();
+  if (roleA) __syncthreads();
 
-  // Epilogue: lane = key, registers = head-dim rows of dK^T / dV^T.
+  // Epilogue: lane = key, registers = head-dim rows of dV^T (A) / dK^T (B).
   if (key >= N) return;
-  T* dkrow = dK + (size_t)key * D;
-  T* dvrow = dV + (size_t)key * D;
-  const float sc = a.scale;
+  T* row_p = reinterpret_cast<T*>(roleA ? a.dv : a.dk) + kvhead + (size_t)key * D;
+  const float sc_out = roleA ? 1.f : a.scale;
 #pragma unroll
   for (int dt = 0; dt < S::NDT; ++dt)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int d0 = dt * 32 + 8 * g + 4 * half;
-      const f32x16& kk = dkt[dt];
-      const f32x16& vv = dvt[dt];
-      st<u32x2>(dkrow + d0,
-                u32x2{E::bits(kk[4 * g] * sc) | ((uint32_t)E::bits(kk[4 * g + 1] * sc) << 16),
-                      E::bits(kk[4 * g + 2] * sc) | ((uint32_t)E::bits(kk[4 * g + 3] * sc) << 16)});
-      st<u32x2>(dvrow + d0, u32x2{E::bits(vv[4 * g]) | ((uint32_t)E::bits(vv[4 * g + 1]) << 16),
-                                  E::bits(vv[4 * g + 2]) | ((uint32_t)E::bits(vv[4 * g + 3]) << 16)});
+      const f32x16& v = acc[dt];
+      st<u32x2>(row_p + d0, u32x2{E::bits(v[4 * g] * sc_out) | ((uint32_t)E::bits(v[4 * g + 1] * sc_out) << 16),
+                                  E::bits(v[4 * g + 2] * sc_out) | ((uint32_t)E::bits(v[4 * g + 3] * sc_out) << 16)});
     }
 }
 
@@ -1002,12 +1080,13 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)((long long)a.B * a.Hkv * nkt));
     const void* fn;
     if constexpr (sizeof(T) == 2)
-      fn = a.causal ? reinterpret_cast<const void*>(&bwd16_kernel<T, D, true>)
-                    : reinterpret_cast<const void*>(&bwd16_kernel<T, D, false>);
+      fn = a.causal ? reinterpret_cast<const void*>(&bwd_kv16_kernel<T, D, true>)
+                    : reinterpret_cast<const void*>(&bwd_kv16_kernel<T, D, false>);
     else
       fn = a.causal ? reinterpret_cast<const void*>(&bwd_main_kernel<T, D, true>)
                     : reinterpret_cast<const void*>(&bwd_main_kernel<T, D, false>);
-    hipError_t e = hipLaunchKernel(fn, grid, dim3(kThreads), kargs, 0, stream);
+    hipError_t e = hipLaunchKernel(fn, grid, dim3(sizeof(T) == 2 ? kKVThreads : kThreads), kargs, 0,
+                                   stream);
     if (e != hipSuccess) return e;
   }
   if constexpr (sizeof(T) == 2) {

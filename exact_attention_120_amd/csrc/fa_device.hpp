@@ -70,6 +70,11 @@ struct Elem<__bf16> {
     const bf16x2 pr = {(__bf16)a, (__bf16)b};
     return __builtin_bit_cast(uint32_t, pr);
   }
+  // The two values of a packed word (exact).
+  __device__ static inline void unpack_pair(uint32_t w, float& a, float& b) {
+    a = __builtin_bit_cast(float, w << 16);
+    b = __builtin_bit_cast(float, w & 0xffff0000u);
+  }
   __device__ static inline uint16_t bits(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
   }
@@ -106,6 +111,11 @@ struct Elem<_Float16> {
   __device__ static inline uint32_t pack_pair(float a, float b) {
     const f16x2 pr = {(_Float16)a, (_Float16)b};
     return __builtin_bit_cast(uint32_t, pr);
+  }
+  __device__ static inline void unpack_pair(uint32_t w, float& a, float& b) {
+    const f16x2 pr = __builtin_bit_cast(f16x2, w);
+    a = (float)pr[0];
+    b = (float)pr[1];
   }
   __device__ static inline uint16_t bits(float x) {
     return __builtin_bit_cast(uint16_t, (_Float16)x);
