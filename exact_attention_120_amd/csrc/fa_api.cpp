@@ -162,7 +162,7 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
   const size_t rows = (size_t)B * H * N;
-  return round_up(rows * sizeof(float)) + round_up(rows * d * sizeof(float));
+  return round_up(rows * sizeof(float)) + round_up(2 * rows * d * sizeof(float));
 }
 
 int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dO,
@@ -197,9 +197,10 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
 
   char* ws = static_cast<char*>(workspace);
   float* dsum = reinterpret_cast<float*>(ws);
-  float* dq_acc = reinterpret_cast<float*>(ws + round_up(lb));
-  fa::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, dsum, dq_acc,
-                B, H, N, d, scale, exp2_scale(scale), causal, dtype, op.Hkv, op.wl, op.wr};
+  float* scratch = reinterpret_cast<float*>(ws + round_up(lb));
+  fa::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, dsum, scratch,
+                B, H, N, d, scale, exp2_scale(scale), causal, dtype, op.Hkv, op.wl, op.wr,
+                scratch};
   return hip_status(fa::launch_bwd(a, reinterpret_cast<hipStream_t>(stream)));
 }
 

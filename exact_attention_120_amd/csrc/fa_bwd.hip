@@ -32,6 +32,7 @@ namespace fa {
 namespace {
 
 constexpr int kThreads = 256;  // 4 waves
+constexpr int kCUs = 256;      // compute units of the part (grid sizing)
 constexpr int kBN = 128;       // keys per workgroup (32 per wave)
 
 template <typename T, int D>
@@ -478,11 +479,15 @@ __global__ __launch_bounds__(kKVThreads, 1) void bwd_kv16_kernel(BwdArgs a) {
 
   const int N = a.N;
   const int nkt = (N + kBN - 1) / kBN;
+  const int parts = a.kv_parts;  // workgroups sharing one key tile's query heads
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int bkv = lin / nkt;  // batch * Hkv + K/V head
-  const int k0 = (lin % nkt) * kBN;
-  const int grp = a.H / a.Hkv;  // query heads sharing this K/V head
-  const int bq0 = (bkv / a.Hkv) * a.H + (bkv % a.Hkv) * grp;  // the first of them
+  const int bkv = lin / (nkt * parts);  // batch * Hkv + K/V head
+  const int k0 = lin % (nkt * parts) / parts * kBN;
+  const int part = lin % parts;
+  const int grp = a.H / a.Hkv / parts;  // query heads of this workgroup
+  // The first of them: the K/V head's group starts at query head
+  // b*H + kvh*(H/Hkv); this part takes the grp heads after part*grp.
+  const int bq0 = (bkv / a.Hkv) * a.H + (bkv % a.Hkv) * (a.H / a.Hkv) + part * grp;
 
   const size_t kvhead = (size_t)bkv * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
@@ -725,9 +730,24 @@ __global__ __launch_bounds__(kKVThreads, 1) void bwd_kv16_kernel(BwdArgs a) {
   if (roleA) __syncthreads();
 
   // Epilogue: lane = key, registers = head-dim rows of dV^T (A) / dK^T (B).
+  // With several parts per key tile, float32 partials go to the scratch
+  // ([part][B*Hkv][N][d], dK then dV) for bwd_kvsum to add up.
   if (key >= N) return;
-  T* row_p = reinterpret_cast<T*>(roleA ? a.dv : a.dk) + kvhead + (size_t)key * D;
   const float sc_out = roleA ? 1.f : a.scale;
+  if (parts > 1) {
+    const size_t plane = (size_t)a.B * a.Hkv * N * D;
+    float* prow = a.dkv_part + (roleA ? (size_t)parts * plane : 0) + part * plane + kvhead + (size_t)key * D;
+#pragma unroll
+    for (int dt = 0; dt < S::NDT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x16& v = acc[dt];
+        st<f32x4>(prow + dt * 32 + 8 * g + 4 * half,
+                  f32x4{v[4 * g] * sc_out, v[4 * g + 1] * sc_out, v[4 * g + 2] * sc_out, v[4 * g + 3] * sc_out});
+      }
+    return;
+  }
+  T* row_p = reinterpret_cast<T*>(roleA ? a.dv : a.dk) + kvhead + (size_t)key * D;
 #pragma unroll
   for (int dt = 0; dt < S::NDT; ++dt)
 #pragma unroll
@@ -737,6 +757,27 @@ __global__ __launch_bounds__(kKVThreads, 1) void bwd_kv16_kernel(BwdArgs a) {
       st<u32x2>(row_p + d0, u32x2{E::bits(v[4 * g] * sc_out) | ((uint32_t)E::bits(v[4 * g + 1] * sc_out) << 16),
                                   E::bits(v[4 * g + 2] * sc_out) | ((uint32_t)E::bits(v[4 * g + 3] * sc_out) << 16)});
     }
+}
+
+// dK, dV = the sum of the parts' float32 partials (in part order, so the
+// result does not depend on scheduling), rounded to T. 4 elements per
+// thread; the first half of the grid does dK, the second dV.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void bwd_kvsum_kernel(BwdArgs a, long long n4) {
+  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= 2 * n4) return;
+  const bool is_v = i >= n4;
+  const long long e = (is_v ? i - n4 : i) * 4;
+  const size_t plane = (size_t)n4 * 4;
+  const float* src = a.dkv_part + (is_v ? (size_t)a.kv_parts * plane : 0) + e;
+  f32x4 s = ld<f32x4>(src);
+  for (int p = 1; p < a.kv_parts; ++p) {
+    const f32x4 x = ld<f32x4>(src + p * plane);
+    s = f32x4{s[0] + x[0], s[1] + x[1], s[2] + x[2], s[3] + x[3]};
+  }
+  const uint32_t w0 = Elem<T>::bits(s[0]) | ((uint32_t)Elem<T>::bits(s[1]) << 16);
+  const uint32_t w1 = Elem<T>::bits(s[2]) | ((uint32_t)Elem<T>::bits(s[3]) << 16);
+  st<u32x2>(reinterpret_cast<T*>(is_v ? a.dv : a.dk) + e, u32x2{w0, w1});
 }
 
 // ---------------------------------------------------------------------------
@@ -1074,10 +1115,21 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
                                    dim3(kThreads), kargs, 0, stream);
     if (e != hipSuccess) return e;
   }
+  // Grouped K/V heads with few K/V heads: split each group's query heads
+  // over up to grp workgroups per key tile until the grid covers the
+  // compute units (16-bit types; the parts' dK/dV are summed afterwards).
+  const int nkt = (a.N + kBN - 1) / kBN;
+  if constexpr (sizeof(T) == 2) {
+    const int grp = a.H / a.Hkv;
+    int parts = 1;
+    while (parts * 2 <= grp && grp % (parts * 2) == 0 &&
+           (long long)a.B * a.Hkv * nkt * parts < kCUs)
+      parts *= 2;
+    args.kv_parts = parts;
+  }
   {
     void* kargs[] = {&args};
-    const int nkt = (a.N + kBN - 1) / kBN;
-    const dim3 grid((unsigned)((long long)a.B * a.Hkv * nkt));
+    const dim3 grid((unsigned)((long long)a.B * a.Hkv * nkt * args.kv_parts));
     const void* fn;
     if constexpr (sizeof(T) == 2)
       fn = a.causal ? reinterpret_cast<const void*>(&bwd_kv16_kernel<T, D, true>)
@@ -1087,6 +1139,14 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
                     : reinterpret_cast<const void*>(&bwd_main_kernel<T, D, false>);
     hipError_t e = hipLaunchKernel(fn, grid, dim3(sizeof(T) == 2 ? kKVThreads : kThreads), kargs, 0,
                                    stream);
+    if (e != hipSuccess) return e;
+  }
+  if constexpr (sizeof(T) == 2) if (args.kv_parts > 1) {
+    long long n4 = (long long)a.B * a.Hkv * a.N * D / 4;
+    void* kargs[] = {&args, &n4};
+    const dim3 grid((unsigned)((2 * n4 + kThreads - 1) / kThreads));
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_kvsum_kernel<T>), grid,
+                                   dim3(kThreads), kargs, 0, stream);
     if (e != hipSuccess) return e;
   }
   if constexpr (sizeof(T) == 2) {

@@ -53,6 +53,11 @@ struct BwdArgs {
   int dtype;
   int Hkv;     // K/V heads (divides H)
   int wl, wr;  // window bounds (negative: unbounded)
+  // float32 scratch of 2 * B*H*N*d elements (16-bit types, grouped K/V
+  // heads): when the query heads of a group are split over several
+  // workgroups, each part's dK and dV land here before being summed.
+  float* dkv_part = nullptr;
+  int kv_parts = 1;  // workgroups per key tile (set by the launcher)
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);

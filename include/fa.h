@@ -97,10 +97,12 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            void* stream);
 
 /*
- * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs:
- * a float32 [B,H,N] row term D_i = sum_k dO_ik O_ik and a float32
- * [B,H,N,d] dQ accumulator, each 256-byte aligned. Returns 0 for invalid
- * sizes.
+ * fa_bwd_workspace_size -- bytes of device workspace fa_bwd (and
+ * fa_bwd_ex) needs: a float32 [B,H,N] row term D_i = sum_k dO_ik O_ik and
+ * a float32 scratch of 2*B*H*N*d elements, each 256-byte aligned. The
+ * scratch holds the dQ accumulator (FA_F32) or, with grouped K/V heads whose
+ * query heads are split over several workgroups, their partial dK and dV
+ * (FA_F16, FA_BF16). Returns 0 for invalid sizes.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
 

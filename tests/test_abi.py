@@ -80,7 +80,7 @@ def test_workspace_size(lib):
     B, H, N, d = 2, 3, 100, 64
     rows = B * H * N
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    assert lib.fa_bwd_workspace_size(B, H, N, d) == up(rows * 4) + up(rows * d * 4)
+    assert lib.fa_bwd_workspace_size(B, H, N, d) == up(rows * 4) + up(2 * rows * d * 4)
     assert lib.fa_bwd_workspace_size(0, H, N, d) == 0
     assert lib.fa_bwd_workspace_size(B, H, N, 80) == 0
 
