@@ -272,7 +272,9 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(F
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
     }
-    const float mc = m * c;
+    // Clamped: with no visible key yet (m = -FLT_MAX) and c > 1 the product
+    // overflows, and -inf + inf would turn hidden scores into NaN.
+    const float mc = fmaxf(m * c, -FLT_MAX);
 
     // Probabilities -> MFMA B operands (P^T), in register order.
     Raw pf[S::NMT * (16 / KH)];
@@ -590,7 +592,9 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a) {
     float p[2 * 16];
     float ls;
     auto exps = [&]() {
-      const float mc = m * c;
+      // Clamped: with no visible key yet (m = -FLT_MAX) and c > 1 the product
+      // overflows, and -inf + inf would turn hidden scores into NaN.
+      const float mc = fmaxf(m * c, -FLT_MAX);
 #pragma unroll
       for (int mt = 0; mt < S::NMT; ++mt)
 #pragma unroll

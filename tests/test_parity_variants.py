@@ -54,7 +54,7 @@ def bwd(inp, causal, scale, window):
     return dq, dk, dv
 
 
-def check_fwd(o, lse, inp, causal, scale, window, dtype, rows=None):
+def check_fwd(o, lse, inp, causal, scale, window, dtype, rows=None, tol_o=TOL_O):
     q, k, v = (to_f64(inp[n]) for n in ("q", "k", "v"))
     if rows is None:
         ref_o, ref_l = attention_forward(q, k, v, scale, causal, window=window)
@@ -65,7 +65,7 @@ def check_fwd(o, lse, inp, causal, scale, window, dtype, rows=None):
         o64, l64 = to_f64(o)[..., rows, :], to_f64(lse)[..., rows]
     assert np.isfinite(o64).all() and np.isfinite(l64).all()
     err_o, err_l = np.abs(o64 - ref_o).max(), np.abs(l64 - ref_l).max()
-    assert err_o <= TOL_O[dtype], f"O max err {err_o:.3e}"
+    assert err_o <= tol_o[dtype], f"O max err {err_o:.3e}"
     assert err_l <= TOL_LSE, f"LSE max err {err_l:.3e}"
     return err_o, err_l
 
@@ -122,6 +122,28 @@ def test_grouped_window_forward_longer(dtype, causal):
     for window in [(256, 0), (70, 130), (5, -1)]:
         o, lse = fwd(inp, causal, scale, window)
         check_fwd(o, lse, inp, causal, scale, window, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_forward_large_scale(dtype, causal):
+    """scale * log2(e) > 1 with a left window bound: rows whose first visited
+    key tile holds none of their keys still have no reference max there
+    (-FLT_MAX), whose product with the exponent multiplier overflows. The
+    result must stay the finite attention (also split over key slices).
+
+    fp32's 1e-5 is the bound at scale 1/sqrt(d); float32 score errors grow
+    with the scores, so at larger scales it is multiplied by scale*sqrt(d)."""
+    print(f"\n[fwd window large scale] dtype={dtype} causal={causal}", flush=True)
+    inp = make_inputs(1, 2, 700, 64, dtype, seed=23)
+    for scale, window in [(1.5, (100, 0)), (4.0, (100, 40)), (1.0, (45, -1))]:
+        tol = {**TOL_O, "f32": TOL_O["f32"] * max(1.0, scale * 64 ** 0.5)}
+        o, lse = fwd(inp, causal, scale, window)
+        check_fwd(o, lse, inp, causal, scale, window, dtype, tol_o=tol)
+        q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+        o, lse = fa.forward(q, k, v, causal=causal, scale=scale, window=window, num_splits=3)
+        torch.cuda.synchronize()
+        check_fwd(o, lse, inp, causal, scale, window, dtype, tol_o=tol)
 
 
 def sampled_rows(N, n, seed):
