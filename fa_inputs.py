@@ -15,6 +15,9 @@ Recipe (the same for every workload):
     N=4096 workload; a power of two, so it commutes exactly with rounding);
   * a round-to-nearest-even cast to the workload's dtype (torch's cast).
 
+8-bit float inputs (``make_fp8_inputs``) start from the same float32 draws
+and store each tensor as OCP E4M3 codes with one per-tensor factor.
+
 The named workloads are the five shapes the scope names: a tiny fp32 head, a
 causal bf16 head batch at N=1024, a non-causal bf16 batch at N=4096 with
 inputs scaled by 0.5, a long-sequence bf16 batch at N=16384 (non-causal and
@@ -97,6 +100,32 @@ def make_inputs(B: int, H: int, N: int, d: int, dtype: str, *, seed: int = 0,
         if input_scale != 1.0:
             x = x * input_scale
         out[name] = x.to(_DTYPES[dtype]).contiguous()
+    return out
+
+
+E4M3_MAX = 448.0  # largest finite OCP E4M3 value
+
+
+def make_fp8_inputs(B: int, H: int, N: int, d: int, *, seed: int = 0,
+                    kv_heads: int | None = None) -> dict:
+    """Q, K, V as OCP E4M3 codes with one dequantization factor per tensor.
+
+    The same float32 draws as ``make_inputs`` (same generator, order and
+    shapes); each tensor x is then stored as codes of x / s with
+    s = max|x| / 448 (float32), so its largest magnitude maps onto E4M3's
+    largest finite value: torch's round-to-nearest-even cast to
+    float8_e4m3fn. Returns uint8 CPU tensors ``q8``, ``k8``, ``v8`` and the
+    factors ``descale`` = (s_q, s_k, s_v) as Python floats.
+    """
+    x = make_inputs(B, H, N, d, "f32", seed=seed, kv_heads=kv_heads)
+    out, descale = {}, []
+    for name in ("q", "k", "v"):
+        t = x[name]
+        s = torch.tensor(float(t.abs().max()) / E4M3_MAX, dtype=torch.float32)
+        codes = (t / s).clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+        out[name + "8"] = codes.view(torch.uint8).contiguous()
+        descale.append(float(s))
+    out["descale"] = tuple(descale)
     return out
 
 

@@ -12,3 +12,4 @@ from .attention import (  # noqa: F401
     attention_probabilities,
     merge_partials,
 )
+from .e4m3 import attention_forward_e4m3, e4m3_decode  # noqa: F401

@@ -176,11 +176,12 @@ def attention_forward(q, k, v, scale: float, causal: bool, q_positions=None, win
                           [q, k, v], 2))
 
 
-def attention_probabilities(q, k, scale: float, causal: bool, window=None):
-    """P = softmax(scale * Q K^T) materialized ([..., N, N]; tests only)."""
+def attention_probabilities(q, k, scale: float, causal: bool, window=None, q_positions=None):
+    """P = softmax(scale * Q K^T) materialized ([..., rows, N]; tests only).
+    With ``q_positions``, q holds only those rows (their sequence positions)."""
     q, k = _f64(q), _f64(k)
     k, _ = _expand_kv(q, k, k)
-    pos = np.arange(q.shape[-2])
+    pos = np.arange(q.shape[-2]) if q_positions is None else np.asarray(q_positions)
 
     def one(a, b):
         s = _scores(a, b, scale, _visible(pos, b.shape[0], causal, window))
