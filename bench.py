@@ -29,8 +29,9 @@ reported in the same unit.
 Other modes (used to collect the rocprofv3 summaries under profiles/):
   --only fwd|bwd        time only that direction (no CPU baseline)
   --sweep               forward over N in {1k,2k,4k,8k,16k}, B=1 H=16 d=128
-  --variants            split-KV, grouped K/V heads and a local window against
-                        the plain calls (one JSON line per case)
+  --variants            split-KV, grouped K/V heads, a local window and the
+                        8-bit float forward against the plain calls (one JSON
+                        line per case)
   --copy-bytes BYTES    a plain device copy of BYTES bytes (counter scaling)
   --summarize DIR       turn rocprofv3 output under DIR into a text table
 """
@@ -52,6 +53,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd/bwd TFLOP/s (bf16, N=4k-16k, d=128) and % of MFMA peak"
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}  # MI355X dense MFMA
+PEAK_FP8_TFLOPS = 5033.2  # MI355X dense FP8 (E4M3) MFMA
 KERNEL_SOURCES = {
     "fwd": ["exact_attention_120_amd/csrc/fa_fwd.hip", "exact_attention_120_amd/csrc/fa_device.hpp"],
     "bwd": ["exact_attention_120_amd/csrc/fa_bwd.hip", "exact_attention_120_amd/csrc/fa_device.hpp"],
@@ -195,7 +197,7 @@ def run_main(args):
     j, roofs = 0, {}
     for name, on, fl, kern in (
             ("fwd", do_fwd, fwd_flop, "fwd_pp_kernel (the one kernel of fa_fwd)"),
-            ("bwd", do_bwd, bwd_flop, "fa_bwd call: bwd_pre_kernel (D, <1%) + bwd16_kernel"
+            ("bwd", do_bwd, bwd_flop, "fa_bwd call: bwd_pre_kernel (D, <1%) + bwd_kv16_kernel"
                                       " (dK, dV) + bwd_dq16_kernel (dQ)")):
         if not on:
             continue
@@ -236,7 +238,8 @@ def run_variants(args):
     """Time the variant rows against the plain calls (HIP events on the
     current stream, back-to-back calls with preallocated buffers): split-KV
     on short/few-head shapes, grouped K/V heads and a local window at
-    N = 16384. One JSON line per case."""
+    N = 16384, and the E4M3 forward against the bf16 one. One JSON line per
+    case."""
     import torch
 
     import exact_attention_120_amd as fa
@@ -307,6 +310,27 @@ def run_variants(args):
                           "fwd_tflops": fl / (f_ms * 1e-3) / 1e12,
                           "bwd_tflops": 2.5 * fl / (b_ms * 1e-3) / 1e12}), flush=True)
 
+    # 8-bit float forward (E4M3 Q, K, V, bf16 O) against the bf16 forward on
+    # the same shape. Peak: MI355X dense FP8 MFMA, 5.0 PFLOP/s.
+    from fa_inputs import make_fp8_inputs
+    for (B, H, N, d, causal) in ((1, 16, 16384, 128, False), (1, 16, 16384, 128, True),
+                                 (4, 16, 4096, 128, False), (2, 16, 4096, 64, False)):
+        x = make_fp8_inputs(B, H, N, d, seed=0)
+        q8, k8, v8 = (x[n].to(dev) for n in ("q8", "k8", "v8"))
+        inp = make_inputs(B, H, N, d, "bf16", seed=0)
+        q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+        o, lse = torch.empty_like(q), torch.empty((B, H, N), device=dev)
+        sc = d ** -0.5
+        fl = 4.0 * B * H * N * N * d / (2 if causal else 1)
+        f8_ms = per_call_ms(lambda: fa.fa_fwd_fp8(q8, k8, v8, o, lse, sc, causal, *x["descale"]))
+        b16_ms = per_call_ms(lambda: fa.fa_fwd(q, k, v, o, lse, sc, causal))
+        print(json.dumps({"case": "fp8_fwd", "B": B, "H": H, "N": N, "d": d, "causal": causal,
+                          "fp8_ms": f8_ms, "bf16_ms": b16_ms,
+                          "fp8_tflops": fl / (f8_ms * 1e-3) / 1e12,
+                          "fp8_frac_of_peak": fl / (f8_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
+                          "bf16_tflops": fl / (b16_ms * 1e-3) / 1e12,
+                          "speedup_vs_bf16": b16_ms / f8_ms}), flush=True)
+
 
 def run_copy(args):
     import torch
@@ -322,7 +346,9 @@ def run_copy(args):
 
 def _short(name: str) -> str:
     """Readable kernel name from a (possibly mangled) symbol."""
-    m = re.search(r"(fwd_pp_kernel|fwd_kernel|fwd_merge_kernel|bwd16_kernel|bwd_main_kernel|"
+    m = re.search(r"(fwd_pp_kernel|fwd_fp8_kernel|fwd_kernel|fwd_merge_kernel|bwd_kv16_kernel|"
+                  r"bwd_kvsum_kernel|"
+                  r"bwd_main_kernel|"
                   r"bwd_pre_kernel|bwd_dq16_kernel|bwd_dq_kernel)I(.*?)EEv", name)
     if m:
         args = m.group(2).replace("DF16b", "bf16,").replace("DF16_", "f16,").replace("f", "f32,", 1)\

@@ -10,7 +10,8 @@ fallback: if libfa.so is missing, or a tensor is not on the GPU, these raise.
 
 Grouped K/V heads are expressed by the shape of k and v ([B, Hkv, N, d] with
 Hkv dividing H); a local window by ``window=(left, right)`` where a negative
-(or None) bound is unbounded on that side.
+(or None) bound is unbounded on that side. ``fa_fwd_fp8``/``forward_fp8``
+take Q, K, V as OCP FP8 E4M3 codes with one dequantization factor each.
 """
 
 from __future__ import annotations
@@ -24,10 +25,13 @@ from . import _lib
 
 __all__ = ["FaError", "fa_fwd", "fa_bwd", "fa_fwd_ex", "fa_bwd_ex", "fa_bwd_workspace_size",
            "fa_fwd_num_splits", "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv",
-           "fa_strerror", "forward", "backward", "DTYPES"]
+           "fa_fwd_fp8", "fa_strerror", "forward", "forward_fp8", "backward", "DTYPES",
+           "FP8_DTYPES"]
 
 DTYPES = {torch.float32: _lib.FA_F32, torch.float16: _lib.FA_F16,
           torch.bfloat16: _lib.FA_BF16}
+# Tensor types accepted as E4M3 codes by fa_fwd_fp8 (the bytes are used as is).
+FP8_DTYPES = (torch.float8_e4m3fn, torch.uint8)
 
 
 class FaError(RuntimeError):
@@ -185,6 +189,49 @@ def fa_fwd_splitkv(q, k, v, o, lse, scale: float, causal: bool, num_splits: int,
                                         int(num_splits), ws_ptr, ws_bytes, _stream(q, stream))
     if st != _lib.FA_OK:
         raise FaError(st, "fa_fwd_splitkv")
+
+
+def fa_fwd_fp8(q8, k8, v8, o, lse, scale: float, causal: bool, q_descale: float,
+               k_descale: float, v_descale: float, window=None, stream=None) -> None:
+    """Enqueue the 8-bit forward: q8, k8, v8 hold E4M3 codes (float8_e4m3fn or
+    uint8 tensors; k8, v8 [B, Hkv, N, d]); o (bf16 or fp16) and lse receive
+    the attention of the dequantized values descale * code."""
+    if q8.dim() != 4:
+        raise ValueError("q8 must be [B, H, N, d]")
+    B, H, N, d = tuple(q8.shape)
+    if k8.dim() != 4 or k8.shape[1] < 1 or H % k8.shape[1]:
+        raise ValueError(f"k8: expected [B, Hkv, N, d] with Hkv dividing H={H}")
+    Hkv = k8.shape[1]
+    for name, t, shape in (("q8", q8, (B, H, N, d)), ("k8", k8, (B, Hkv, N, d)),
+                           ("v8", v8, (B, Hkv, N, d))):
+        if not t.is_cuda or t.dtype not in FP8_DTYPES or tuple(t.shape) != shape \
+                or not t.is_contiguous():
+            raise ValueError(f"{name}: expected contiguous {shape} float8_e4m3fn/uint8 GPU tensor,"
+                             f" got {tuple(t.shape)} {t.dtype}")
+    if o.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("o must be bfloat16 or float16")
+    _check({"o": o}, (B, H, N, d), o.dtype)
+    _check({"lse": lse}, (B, H, N), torch.float32)
+    opts = _options(Hkv, window)
+    with torch.cuda.device(q8.device):
+        st = _lib.load().fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o.data_ptr(),
+                                    lse.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
+                                    float(q_descale), float(k_descale), float(v_descale),
+                                    DTYPES[o.dtype], ctypes.byref(opts), _stream(q8, stream))
+    if st != _lib.FA_OK:
+        raise FaError(st, "fa_fwd_fp8")
+
+
+def forward_fp8(q8, k8, v8, descale=(1.0, 1.0, 1.0), causal: bool = False,
+                scale: float | None = None, out_dtype=torch.bfloat16, window=None, stream=None):
+    """Allocate O (``out_dtype``) and LSE with torch and run fa_fwd_fp8;
+    ``descale`` = (q_descale, k_descale, v_descale). Returns (o, lse)."""
+    B, H, N, d = tuple(q8.shape)
+    o = torch.empty((B, H, N, d), dtype=out_dtype, device=q8.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    fa_fwd_fp8(q8, k8, v8, o, lse, _default_scale(d, scale), causal, *descale, window=window,
+               stream=stream)
+    return o, lse
 
 
 def _plain(q, k, window) -> bool:

@@ -38,6 +38,8 @@ SIGNATURES = {
     "fa_fwd_splitkv_workspace_size": (_sz, [_int, _int, _int, _int, _int, _int]),
     "fa_fwd_splitkv": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _flt, _int, _int,
                               _opt, _int, _vp, _sz, _vp]),
+    "fa_fwd_fp8": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _flt, _int, _flt, _flt,
+                          _flt, _int, _opt, _vp]),
     "fa_strerror": (_c.c_char_p, [_int]),
 }
 

@@ -101,6 +101,39 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   return fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, nullptr, stream);
 }
 
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int N, int d, float scale, int causal, float q_descale, float k_descale,
+               float v_descale, int out_dtype, const fa_options* opts, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (out_dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (out_dtype != FA_F16 && out_dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+  int st = check_shape(B, H, N, d, scale, causal, out_dtype);
+  if (st != FA_OK) return st;
+  const float descales[] = {q_descale, k_descale, v_descale};
+  for (float x : descales)
+    if (!isfinite(x) || !(x > 0.f)) return FA_ERR_INVALID_ARG;
+  const float score_scale = scale * q_descale * k_descale;
+  if (!isfinite(score_scale)) return FA_ERR_INVALID_ARG;
+  Opts op;
+  if ((st = read_opts(opts, H, &op)) != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  const size_t qb = (size_t)B * H * N * d;
+  const size_t kb = (size_t)B * op.Hkv * N * d;
+  const size_t ob = qb * elem_size(out_dtype);
+  const size_t lb = (size_t)B * H * N * sizeof(float);
+  struct Range { const void* p; size_t n; };
+  const Range ins[] = {{q, qb}, {k, kb}, {v, kb}};
+  for (const Range& in : ins)
+    if (overlap(o, ob, in.p, in.n) || overlap(lse, lb, in.p, in.n)) return FA_ERR_INVALID_ARG;
+  if (overlap(o, ob, lse, lb)) return FA_ERR_INVALID_ARG;
+
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, score_scale, exp2_scale(score_scale), causal,
+                out_dtype, op.Hkv, op.wl, op.wr};
+  a.v_descale = v_descale;
+  return hip_status(fa::launch_fwd_fp8(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
 int fa_fwd_num_splits(int B, int H, int N, int d, int dtype) {
   if (check_shape(B, H, N, d, 1.f, 0, dtype) != FA_OK) return 0;
   return fa::fwd_auto_splits(B, H, N, dtype);

@@ -30,6 +30,10 @@ struct FwdArgs {
   int num_splits = 1;
   float* o_part = nullptr;
   float* lse_part = nullptr;
+  // 8-bit inputs (launch_fwd_fp8): O is multiplied by this dequantization
+  // factor of V; scale / scale_log2 then already hold the product of the
+  // softmax scale and the factors of Q and K.
+  float v_descale = 1.f;
 };
 
 // Backward: forward tensors plus dO and the gradient outputs. `dsum` is the
@@ -61,6 +65,8 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+// E4M3 q, k, v (bytes); a.dtype is the output type (fp16 or bf16).
+hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 
 long long fwd_grid_size(int B, int H, int N);

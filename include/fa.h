@@ -224,6 +224,46 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    const fa_options* opts, int num_splits, void* workspace,
                    size_t workspace_bytes, void* stream);
 
+/*
+ * 8-bit float forward.
+ *
+ * The pages list lower-precision data types (FP8, INT8) among the method's
+ * next steps (section "应用展望" of "FlashAttention与新一代硬件架构融合：
+ * 解锁大模型训练新高度") without a
+ * scheme. This entry point reads Q, K and V as OCP FP8 E4M3 codes (1 sign,
+ * 4 exponent bits with bias 7, 3 mantissa bits; no infinities; 0x7F and 0xFF
+ * are NaN; largest finite value 448), each tensor with one dequantization
+ * factor, and computes the attention of fa_fwd_ex over the values those
+ * codes stand for:
+ *   Q = q_descale * Q8, K = k_descale * K8, V = v_descale * V8,
+ *   O = softmax(scale * Q K^T [causal rule, window]) V,  LSE as for fa_fwd.
+ * The score products and the P V product run on the gfx950 FP8 matrix cores
+ * with float32 accumulation; the softmax is float32 and its probabilities
+ * enter the P V product as E4M3 codes (relative rounding 2^-4 each), the
+ * normalizer and LSE are taken from the unrounded values. See the parity
+ * tests for the error bound this implies.
+ *
+ * fa_fwd_fp8
+ *   q        : [B, H, N, d] E4M3 codes (one byte each), device memory.
+ *   k, v     : [B, Hkv, N, d] E4M3 codes (Hkv from opts->kv_heads, default H).
+ *   o        : [B, H, N, d] output in ``out_dtype`` (FA_BF16 or FA_F16).
+ *   lse      : [B, H, N] float32 output, natural log.
+ *   q_descale, k_descale, v_descale : finite, > 0.
+ *   scale    : softmax scale, finite, >= 0 (the scores use
+ *              scale * q_descale * k_descale, which must be finite).
+ *   causal, opts, stream : as for fa_fwd_ex (opts may be NULL).
+ * All pointers 16-byte aligned; outputs must not overlap inputs or each
+ * other. Inputs must not hold NaN codes (a NaN anywhere in a visited tile
+ * can reach every row of that tile). The result for every row is written;
+ * nothing is allocated. Status: as fa_fwd_ex, plus out_dtype not FA_BF16 or
+ * FA_F16 -> FA_ERR_INVALID_ARG (FA_F32 -> FA_ERR_UNSUPPORTED), a descale
+ * not finite and positive -> FA_ERR_INVALID_ARG.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal,
+               float q_descale, float k_descale, float v_descale, int out_dtype,
+               const fa_options* opts, void* stream);
+
 /* fa_strerror -- static, NUL-terminated description of a status code. */
 const char* fa_strerror(int status);
 

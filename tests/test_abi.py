@@ -28,7 +28,7 @@ def test_header_functions_are_exported(lib):
     names = _lib.header_functions()
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_fwd_ex", "fa_bwd_ex", "fa_bwd_workspace_size",
                           "fa_fwd_num_splits", "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv",
-                          "fa_strerror"}
+                          "fa_fwd_fp8", "fa_strerror"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -248,3 +248,44 @@ SPLITKV_CASES = [
 @pytest.mark.parametrize("kw,status", SPLITKV_CASES)
 def test_splitkv_rejects(lib, kw, status):
     assert splitkv(lib, **kw) == status
+
+
+def fwd_fp8(lib, q=Q, k=K, v=V, o=O, lse=LSE, B=1, H=4, N=16, d=64, scale=0.125, causal=0,
+            dq=0.01, dk=0.02, dv=0.5, out_dtype=2, kv_heads=0, opts=True):
+    op = ctypes.byref(_lib.FaOptions(kv_heads, -1, -1)) if opts else None
+    return lib.fa_fwd_fp8(q, k, v, o, lse, B, H, N, d, scale, causal, dq, dk, dv, out_dtype, op,
+                          None)
+
+
+QB_FP8 = 1 * 4 * 16 * 64  # bytes of q (one byte per code) in the calls above
+
+FWD_FP8_CASES = [
+    (dict(q=None), FA_ERR_INVALID_ARG),
+    (dict(v=None), FA_ERR_INVALID_ARG),
+    (dict(out_dtype=0), FA_ERR_UNSUPPORTED),   # float32 output is not offered
+    (dict(out_dtype=3), FA_ERR_INVALID_ARG),
+    (dict(out_dtype=-1), FA_ERR_INVALID_ARG),
+    (dict(dq=0.0), FA_ERR_INVALID_ARG),
+    (dict(dk=-1.0), FA_ERR_INVALID_ARG),
+    (dict(dv=float("nan")), FA_ERR_INVALID_ARG),
+    (dict(dv=float("inf")), FA_ERR_INVALID_ARG),
+    (dict(scale=3e38, dq=1e10, dk=1e10), FA_ERR_INVALID_ARG),  # score scale overflows
+    (dict(scale=-1.0), FA_ERR_INVALID_ARG),
+    (dict(causal=5), FA_ERR_INVALID_ARG),
+    (dict(d=256), FA_ERR_UNSUPPORTED),
+    (dict(B=0), FA_ERR_INVALID_ARG),
+    (dict(kv_heads=3), FA_ERR_INVALID_ARG),
+    (dict(q=Q + 8), FA_ERR_ALIGN),
+    (dict(o=O + 2), FA_ERR_ALIGN),
+    # q spans QB_FP8 bytes (1-byte codes): an output starting inside it overlaps.
+    (dict(o=Q + QB_FP8 - 256), FA_ERR_INVALID_ARG),
+    (dict(lse=Q + QB_FP8 - 16), FA_ERR_INVALID_ARG),
+    (dict(lse=O + 256), FA_ERR_INVALID_ARG),   # lse inside o (bf16: twice q's bytes)
+    (dict(opts=False, d=32), FA_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("kw,status", FWD_FP8_CASES)
+def test_fwd_fp8_rejects(lib, kw, status):
+    assert fwd_fp8(lib, **kw) == status
+
