@@ -32,6 +32,7 @@ Other modes (used to collect the rocprofv3 summaries under profiles/):
   --variants            split-KV, grouped K/V heads, a local window and the
                         8-bit float forward against the plain calls (one JSON
                         line per case)
+  --fp8                 the E4M3 forward alone, B=1 H=16 N=16384 d=128
   --copy-bytes BYTES    a plain device copy of BYTES bytes (counter scaling)
   --summarize DIR       turn rocprofv3 output under DIR into a text table
 """
@@ -332,6 +333,37 @@ def run_variants(args):
                           "speedup_vs_bf16": b16_ms / f8_ms}), flush=True)
 
 
+def run_fp8(args):
+    """The E4M3 forward alone at B=1 H=16 N=16384 d=128 (non-causal), timed
+    like the main line; one JSON line (used for its rocprofv3 summaries)."""
+    import torch
+
+    import exact_attention_120_amd as fa
+    from fa_inputs import make_fp8_inputs
+
+    B, H, N, d = 1, 16, 16384, 128
+    dev = torch.device("cuda:0")
+    x = make_fp8_inputs(B, H, N, d, seed=0)
+    q8, k8, v8 = (x[n].to(dev) for n in ("q8", "k8", "v8"))
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    sc = float(torch.tensor(d ** -0.5, dtype=torch.float32))
+
+    def step(ev):
+        if ev is not None:
+            ev[0].record()
+        fa.fa_fwd_fp8(q8, k8, v8, o, lse, sc, False, *x["descale"])
+        if ev is not None:
+            ev[1].record()
+
+    total_ms, per = time_calls(step, args.steps, args.warmup, 1, args.warmup_seconds)
+    ms = sum(per[0]) / len(per[0])
+    tf = 4.0 * B * H * N * N * d / (ms * 1e-3) / 1e12
+    print(json.dumps({"case": "fp8_fwd", "B": B, "H": H, "N": N, "d": d, "causal": False,
+                      "steps": args.steps, "ms_per_call": ms, "tflops": tf,
+                      "frac_of_fp8_peak": tf / PEAK_FP8_TFLOPS}), flush=True)
+
+
 def run_copy(args):
     import torch
 
@@ -350,11 +382,17 @@ def _short(name: str) -> str:
                   r"bwd_kvsum_kernel|"
                   r"bwd_main_kernel|"
                   r"bwd_pre_kernel|bwd_dq16_kernel|bwd_dq_kernel)I(.*?)EEv", name)
+    if m and m.group(1) == "fwd_fp8_kernel":  # <D, CAUSAL, output type>
+        a = m.group(2)
+        d = re.search(r"Li(\d+)E", a)
+        return (f"fwd_fp8_kernel<d={d.group(1) if d else '?'},"
+                f"{'causal' if 'Lb1' in a else 'noncausal'},out="
+                f"{'bf16' if 'DF16b' in a else 'f16'}>")
     if m:
         args = m.group(2).replace("DF16b", "bf16,").replace("DF16_", "f16,").replace("f", "f32,", 1)\
             if m.group(2).startswith("f") else m.group(2).replace("DF16b", "bf16,").replace("DF16_", "f16,")
         args = args.replace("Li", "d=").replace("ELb0", ",noncausal").replace("ELb1", ",causal")
-        return m.group(1) + "<" + args.rstrip("E") + ">"
+        return m.group(1) + "<" + args.rstrip("E").rstrip(",") + ">"
     return name[:70]
 
 
@@ -396,6 +434,7 @@ def main():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--sweep", action="store_true")
     p.add_argument("--variants", action="store_true")
+    p.add_argument("--fp8", action="store_true")
     p.add_argument("--copy-bytes", type=int)
     p.add_argument("--summarize")
     args = p.parse_args()
@@ -412,6 +451,8 @@ def main():
         return run_sweep(args)
     if args.variants:
         return run_variants(args)
+    if args.fp8:
+        return run_fp8(args)
     return run_main(args)
 
 
