@@ -452,12 +452,14 @@ template <int D>
 struct KVShape {
   static constexpr int ROWB = D * 2;
   static constexpr int TILE = kStepQ * ROWB;          // Q or dO of one step
-  static constexpr int OFF_DO = TILE;
-  static constexpr int OFF_LSE = 2 * TILE;            // LSE * log2(e), float32
-  static constexpr int OFF_DSUM = 2 * TILE + kStepQ * 4;
-  static constexpr int STAGE = 2 * TILE + 2 * kStepQ * 4;
   static constexpr int NSTAGE = 3;
-  static constexpr int OFF_PX = NSTAGE * STAGE;       // P exchange: 4 slices x 4 KB
+  // Tensor-major regions, so that a step's stage adds at most 2 * TILE to a
+  // region base (within the 16-bit offset of LDS instructions).
+  static constexpr int REG_Q = 0;                     // Q tiles of the stages
+  static constexpr int REG_DO = NSTAGE * TILE;        // dO tiles
+  static constexpr int REG_LSE = 2 * NSTAGE * TILE;   // LSE * log2(e), float32
+  static constexpr int REG_DSUM = REG_LSE + NSTAGE * kStepQ * 4;
+  static constexpr int OFF_PX = REG_DSUM + NSTAGE * kStepQ * 4;  // P exchange: 4 slices x 4 KB
   static constexpr int LDS = OFF_PX + 4 * 4096;
   static constexpr int UNITS = D / 8;
   static constexpr int NLD = kStepQ * UNITS / 256;    // loads per thread (one tensor, one role)
@@ -468,14 +470,23 @@ struct KVShape {
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kKVThreads, 1) void bwd_kv16_kernel(BwdArgs a) {
+template <int K>
+struct IntC {
+  static constexpr int value = K;
+};
+
+// One role's whole program. The role and, inside the main loop, the stage
+// buffer of each step are compile-time constants, so every LDS address is a
+// loop-invariant per-lane base plus an immediate offset: with a runtime
+// stage index the matrix phase re-added the stage and role offsets to each
+// of its address registers (about as many VALU instructions as MFMAs).
+template <typename T, int D, bool CAUSAL, bool ROLE_A>
+__device__ __forceinline__ void kv16_role(const BwdArgs& a, char* lds) {
   using S = KVShape<D>;
   using E = Elem<T>;
   using Raw = u32x4;
   constexpr int ROWB = S::ROWB;
-
-  __shared__ __attribute__((aligned(16))) char lds[S::LDS];
+  constexpr bool roleA = ROLE_A;
 
   const int N = a.N;
   const int nkt = (N + kBN - 1) / kBN;
@@ -497,7 +508,6 @@ __global__ __launch_bounds__(kKVThreads, 1) void bwd_kv16_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool roleA = wave < 4;
   const int slice = wave & 3;       // the 32-key slice this wave serves
   const int col = lane & 31, half = lane >> 5;
   const int kw0 = k0 + slice * 32;  // first key of the slice
@@ -538,6 +548,14 @@ __global__ __launch_bounds__(kKVThreads, 1) void bwd_kv16_kernel(BwdArgs a) {
   // Stage staging, split by role: role A streams Q and LSE, role B dO and
   // D (each 256 threads; rows past N read as zeros, LSE = +inf there so
   // their probabilities are exactly 0).
+  // Region offsets of this role: the tile it reads row-wise (and stages),
+  // the tile it reads transposed, and its row statistics. Kept opaque so
+  // that the compiler adds them into the loop-invariant per-lane base
+  // addresses and leaves only stage and operand offsets for the immediates.
+  int ts_off = roleA ? S::REG_Q : S::REG_DO;
+  int ta_off = roleA ? S::REG_DO : S::REG_Q;
+  int stat_off = roleA ? S::REG_LSE : S::REG_DSUM;
+  asm volatile("" : "+s"(ts_off), "+s"(ta_off), "+s"(stat_off));
   const int rtid = tid & 255;
   u32x4 sx[S::NLD];
   float stat = 0.f;
@@ -555,17 +573,17 @@ __global__ __launch_bounds__(kKVThreads, 1) void bwd_kv16_kernel(BwdArgs a) {
       stat = roleA ? (row < N ? a.lse[qh + row] * kLog2e : INFINITY) : (row < N ? a.dsum[qh + row] : 0.f);
     }
   };
-  auto store = [&](int j) {
-    char* stage = lds + (j % S::NSTAGE) * S::STAGE + (roleA ? 0 : S::OFF_DO);
+  auto store = [&](auto kc) {  // into stage buffer kc
+    char* stage = lds + ts_off + decltype(kc)::value * S::TILE;
 #pragma unroll
     for (int i = 0; i < S::NLD; ++i) {
       const int idx = rtid + 256 * i, row = idx / S::UNITS, u = idx % S::UNITS;
       st<u32x4>(stage + tile_off<ROWB>(row, u * 16), sx[i]);
     }
     if (rtid < kStepQ)
-      st<float>(lds + (j % S::NSTAGE) * S::STAGE + (roleA ? S::OFF_LSE : S::OFF_DSUM) + rtid * 4, stat);
+      st<float>(lds + stat_off + decltype(kc)::value * (kStepQ * 4) + rtid * 4, stat);
   };
-  auto stage_of = [&](int j) -> const char* { return lds + (j % S::NSTAGE) * S::STAGE; };
+  auto stats_at = [&](auto kc) -> const char* { return lds + stat_off + decltype(kc)::value * (kStepQ * 4); };
   char* const px = lds + S::OFF_PX + slice * 4096 + lane * 16;  // this lane's P slots
 
   // Matrix phase of either role: first dV^T += dO^T P (role A) or
@@ -575,11 +593,11 @@ __global__ __launch_bounds__(kKVThreads, 1) void bwd_kv16_kernel(BwdArgs a) {
   // run in chunks of four; the LDS operands of chunk c + 1 are read while
   // chunk c computes. Chunk c < NDT is head-dim block c of the accumulation,
   // chunk NDT + 2 qb + h is query block qb, head-dim operands 4h .. 4h + 3.
-  auto mphase = [&](int ja, int js, auto acc_c, auto sc_c) {
+  auto mphase = [&](auto ka, auto ks, auto acc_c, auto sc_c) {
     constexpr int QKH = S::NQK / 4;
     constexpr int NC = S::NDT + 2 * QKH;
-    const char* ta = stage_of(ja) + (roleA ? S::OFF_DO : 0);
-    const char* ts = stage_of(js) + (roleA ? 0 : S::OFF_DO);
+    const char* ta = lds + ta_off + decltype(ka)::value * S::TILE;
+    const char* ts = lds + ts_off + decltype(ks)::value * S::TILE;
     constexpr int c0 = decltype(acc_c)::value ? 0 : S::NDT;
     constexpr int c1 = decltype(sc_c)::value ? NC : S::NDT;
     Raw op[2][4];
@@ -621,8 +639,8 @@ __global__ __launch_bounds__(kKVThreads, 1) void bwd_kv16_kernel(BwdArgs a) {
   // P^T operands (operand p = 2*qb + u covers registers [8u, 8u+8) of block
   // qb: queries 16p + 4h + 0..3 and 16p + 8 + 4h + 0..3), also stored to the
   // lane's slots for role B.
-  auto probabilities = [&](int j) {
-    const char* stage = stage_of(j);
+  auto probabilities = [&](int j, auto kc) {
+    const char* lse2 = stats_at(kc);
     const int q0 = step_q0(j);
     const bool need_mask =
         !block_all_visible(q0, q0 + kStepQ - 1, kw0, kw0 + 31, N, CAUSAL, a.wl, a.wr);
@@ -641,7 +659,7 @@ __global__ __launch_bounds__(kKVThreads, 1) void bwd_kv16_kernel(BwdArgs a) {
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           const int ql = 32 * qb + 16 * u + 8 * k + 4 * half;  // first of 4 query rows
-          const f32x4 l2 = ld<f32x4>(stage + S::OFF_LSE + ql * 4);
+          const f32x4 l2 = ld<f32x4>(lse2 + ql * 4);
           float pe[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) pe[e] = __builtin_amdgcn_exp2f(fmaf(sc[qb][8 * u + 4 * k + e], c, -l2[e]));
@@ -655,8 +673,8 @@ __global__ __launch_bounds__(kKVThreads, 1) void bwd_kv16_kernel(BwdArgs a) {
   };
   // Role B, step j: dS = P * (dP - D) with P read back from role A's slots,
   // packed as dS^T operands (the same operand layout).
-  auto score_grads = [&](int j) {
-    const char* stage = stage_of(j);
+  auto score_grads = [&](auto kc) {
+    const char* dsum = stats_at(kc);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -666,7 +684,7 @@ __global__ __launch_bounds__(kKVThreads, 1) void bwd_kv16_kernel(BwdArgs a) {
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           const int ql = 32 * qb + 16 * u + 8 * k + 4 * half;
-          const f32x4 dd = ld<f32x4>(stage + S::OFF_DSUM + ql * 4);
+          const f32x4 dd = ld<f32x4>(dsum + ql * 4);
           float pe[4], de[4];
           E::unpack_pair(pw[2 * k], pe[0], pe[1]);
           E::unpack_pair(pw[2 * k + 1], pe[2], pe[3]);
@@ -681,10 +699,10 @@ __global__ __launch_bounds__(kKVThreads, 1) void bwd_kv16_kernel(BwdArgs a) {
 
   // Prologue: stages 0 and 1 in LDS.
   load(0);
-  store(0);
+  store(IntC<0>{});
   if (nsteps > 1) {
     load(1);
-    store(1);
+    store(IntC<1>{});
   }
 #pragma unroll
   for (int i = 0; i < S::NQK; ++i) settle(kvb[i]);
@@ -700,32 +718,53 @@ __global__ __launch_bounds__(kKVThreads, 1) void bwd_kv16_kernel(BwdArgs a) {
   // j+1 in M(j) and stores them in V(j); role B loads dO/D of stage j+2 in
   // M(j) and stores them in V(j). Stage j lives in buffer j % 3; each store
   // lands in a buffer whose last readers passed an earlier barrier.
-  const int ahead = roleA ? 1 : 2;
-  auto vphase = [&](int j) {
-    if (roleA)
-      probabilities(j);
+  constexpr int ahead = roleA ? 1 : 2;
+  auto vphase = [&](int j, auto kc) {
+    if constexpr (roleA)
+      probabilities(j, kc);
     else
-      score_grads(j);
+      score_grads(kc);
   };
   if (!roleA) __syncthreads();
   {
     if (roleA ? false : 2 < nsteps) load(2);
-    mphase(0, 0, BoolC<false>{}, BoolC<true>{});
+    mphase(IntC<0>{}, IntC<0>{}, BoolC<false>{}, BoolC<true>{});
     __syncthreads();
-    vphase(0);
-    if (!roleA && 2 < nsteps) store(2);
+    vphase(0, IntC<0>{});
+    if (!roleA && 2 < nsteps) store(IntC<2>{});
     __syncthreads();
   }
-  for (int j = 1; j < nsteps; ++j) {
+  // Step j (stage buffer kc = j % 3).
+  auto step = [&](int j, auto kc) {
+    constexpr int K = decltype(kc)::value;
     const int ls = j + ahead;
     if (ls < nsteps) load(ls);
-    mphase(j - 1, j, BoolC<true>{}, BoolC<true>{});
+    mphase(IntC<(K + 2) % 3>{}, kc, BoolC<true>{}, BoolC<true>{});
     __syncthreads();
-    vphase(j);
-    if (ls < nsteps) store(ls);
+    vphase(j, kc);
+    if (ls < nsteps) store(IntC<(K + ahead) % 3>{});
     __syncthreads();
+  };
+  // Unrolled by the three stage buffers, straight-line, so that loop-carried
+  // registers need no copies where differently compiled steps would meet.
+  static_assert(S::NSTAGE == 3, "three stage buffers");
+  int j = 1;
+  for (; j + 2 < nsteps; j += 3) {
+    step(j, IntC<1>{});
+    step(j + 1, IntC<2>{});
+    step(j + 2, IntC<0>{});
   }
-  mphase(nsteps - 1, 0, BoolC<true>{}, BoolC<false>{});
+  if (j < nsteps) step(j++, IntC<1>{});
+  if (j < nsteps) step(j++, IntC<2>{});
+  {
+    const int k = (nsteps - 1) % 3;
+    if (k == 0)
+      mphase(IntC<0>{}, IntC<0>{}, BoolC<true>{}, BoolC<false>{});
+    else if (k == 1)
+      mphase(IntC<1>{}, IntC<0>{}, BoolC<true>{}, BoolC<false>{});
+    else
+      mphase(IntC<2>{}, IntC<0>{}, BoolC<true>{}, BoolC<false>{});
+  }
   __syncthreads();
   if (roleA) __syncthreads();
 
@@ -757,6 +796,15 @@ __global__ __launch_bounds__(kKVThreads, 1) void bwd_kv16_kernel(BwdArgs a) {
       st<u32x2>(row_p + d0, u32x2{E::bits(v[4 * g] * sc_out) | ((uint32_t)E::bits(v[4 * g + 1] * sc_out) << 16),
                                   E::bits(v[4 * g + 2] * sc_out) | ((uint32_t)E::bits(v[4 * g + 3] * sc_out) << 16)});
     }
+}
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(kKVThreads, 1) void bwd_kv16_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[KVShape<D>::LDS];
+  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 4)
+    kv16_role<T, D, CAUSAL, true>(a, lds);
+  else
+    kv16_role<T, D, CAUSAL, false>(a, lds);
 }
 
 // dK, dV = the sum of the parts' float32 partials (in part order, so the
