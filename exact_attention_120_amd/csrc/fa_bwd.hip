@@ -841,7 +841,8 @@ __global__ __launch_bounds__(kThreads) void bwd_kvsum_kernel(BwdArgs a, long lon
 // one barrier per phase, group B one phase behind group A. K and V tiles of
 // 32 keys use the swizzled row layout of the key-outer kernel (conflict-free
 // for both 16-byte row reads and transposing reads). K tile i is read in the
-// matrix phases of steps i (S) and i + 1 (dQ), so K has three buffers, V two.
+// matrix phases of steps i (S) and i + 1 (dQ), so K has three buffers (and
+// V three as well, so that both use buffer i % 3).
 // Group A streams K (tile i + 1 loaded in its matrix phase i, stored in its
 // vector phase i); group B streams V (tile i + 2 loaded in its matrix phase
 // i, stored in its vector phase i, which comes before the matrix phase i + 1
@@ -856,7 +857,9 @@ template <int D>
 struct DQShape {
   static constexpr int ROWB = D * 2;
   static constexpr int TILE = kDQBN * ROWB;
-  static constexpr int NKBUF = 3, NVBUF = 2;
+  // Three buffers each, so that the buffer of step i (i % 3) is the same for
+  // K and V and the main loop can be compiled per buffer.
+  static constexpr int NKBUF = 3, NVBUF = 3;
   static constexpr int LDS = (NKBUF + NVBUF) * TILE;
   static constexpr int NQK = D / 16;                     // MFMAs over the head dim
   static constexpr int NDT = D / 32;                     // head-dim blocks of dQ
@@ -1039,6 +1042,9 @@ __global__ __launch_bounds__(kDQThreads, 1) void bwd_dq16_kernel(BwdArgs a) {
   };
   auto kt = [&](int i) -> char* { return kbuf + (i % S::NKBUF) * S::TILE; };
   auto vt = [&](int i) -> char* { return vbuf + (i % S::NVBUF) * S::TILE; };
+  // The same with the buffer a compile-time constant.
+  auto kts = [&](auto bc) -> char* { return kbuf + decltype(bc)::value * S::TILE; };
+  auto vts = [&](auto bc) -> char* { return vbuf + decltype(bc)::value * S::TILE; };
 
   // Prologue: K tile 0 (group A), V tiles 0 and 1 (group B).
   const bool kgrp = group == 0;  // group A streams K, group B V
@@ -1059,11 +1065,10 @@ __global__ __launch_bounds__(kDQThreads, 1) void bwd_dq16_kernel(BwdArgs a) {
   // a vector phase V(i) (dS of tile i), each ending at a barrier; group B
   // runs one phase behind group A (one extra barrier first, A one extra at
   // the end). Group A loads K tile i + 1 in M(i) and stores it in V(i);
-  // group B loads V tile i + 2 in M(i) and stores it in V(i). K tile j lives
-  // in buffer j % 3, V tile j in buffer j % 2; each store lands in a buffer
-  // whose last readers passed an earlier barrier. At step w_lo (> 0) the dQ
-  // half adds the zero initial dS; at step w_end (< nkv) the S, dP half is
-  // unused.
+  // group B loads V tile i + 2 in M(i) and stores it in V(i). K tile j and
+  // V tile j live in buffer j % 3; each store lands in a buffer whose last
+  // readers passed an earlier barrier. At step w_lo (> 0) the dQ half adds
+  // the zero initial dS; at step w_end (< nkv) the S, dP half is unused.
   const HeadBuf& X = kgrp ? K : V;
   if (!kgrp) __syncthreads();
   {
@@ -1075,17 +1080,41 @@ __global__ __launch_bounds__(kDQThreads, 1) void bwd_dq16_kernel(BwdArgs a) {
     if (lt < nkv) lstore(kgrp ? kt(lt) : vt(lt));
     __syncthreads();
   }
-  for (int i = 1; i < nkv; ++i) {
+  // Step i with its buffer b = i % 3 a compile-time constant, so that every
+  // LDS operand address is a loop-invariant base plus an immediate offset
+  // (with a runtime buffer index each matrix phase re-added the buffer
+  // offsets to every operand address).
+  auto step = [&](int i, auto bc) {
+    constexpr int b = decltype(bc)::value;
     const int lt = kgrp ? i + 1 : i + 2;
     if (lt < nkv) gload(X, lt);
-    if (w_lo <= i && i <= w_end) mphase(kt(i - 1), kt(i), vt(i), BoolC<true>{}, BoolC<true>{});
+    if (w_lo <= i && i <= w_end)
+      mphase(kts(IntC<(b + 2) % 3>{}), kts(bc), vts(bc), BoolC<true>{}, BoolC<true>{});
     __syncthreads();
     if (w_lo <= i && i < w_end) vphase((t0 + i) * kDQBN);
-    if (lt < nkv) lstore(kgrp ? kt(lt) : vt(lt));
+    if (lt < nkv) lstore(kgrp ? kts(IntC<(b + 1) % 3>{}) : vts(IntC<(b + 2) % 3>{}));
     __syncthreads();
+  };
+  // Unrolled by the three buffers, straight-line (no register copies where
+  // differently compiled steps would meet).
+  int i = 1;
+  for (; i + 2 < nkv; i += 3) {
+    step(i, IntC<1>{});
+    step(i + 1, IntC<2>{});
+    step(i + 2, IntC<0>{});
   }
+  if (i < nkv) step(i++, IntC<1>{});
+  if (i < nkv) step(i++, IntC<2>{});
   // Final matrix phase: dQ of the last tile.
-  if (w_end == nkv) mphase(kt(nkv - 1), kt(nkv - 1), vt(0), BoolC<true>{}, BoolC<false>{});
+  if (w_end == nkv) {
+    const int b = (nkv - 1) % 3;
+    if (b == 0)
+      mphase(kts(IntC<0>{}), kts(IntC<0>{}), vts(IntC<0>{}), BoolC<true>{}, BoolC<false>{});
+    else if (b == 1)
+      mphase(kts(IntC<1>{}), kts(IntC<1>{}), vts(IntC<0>{}), BoolC<true>{}, BoolC<false>{});
+    else
+      mphase(kts(IntC<2>{}), kts(IntC<2>{}), vts(IntC<0>{}), BoolC<true>{}, BoolC<false>{});
+  }
   __syncthreads();
   if (kgrp) __syncthreads();
 
