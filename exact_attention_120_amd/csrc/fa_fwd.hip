@@ -667,15 +667,24 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a) {
   const HeadBuf& X = kgrp ? K : V;
   const int soff = kgrp ? GS::k_off(gtid) : GS::v_off(gtid);
   const int sstride = kgrp ? GS::K_STRIDE : GS::V_STRIDE;
+  // Where a group issues the global load of the next tile it stores: at
+  // d = 128 right after its previous store, before the barrier (the staging
+  // registers are free from there, and the load gets the barrier wait on top
+  // of a matrix phase to land: measured +2% non-causal, +7% causal); at
+  // d = 64 at the start of the matrix phase that precedes the store
+  // (measured 4% faster there).
+  constexpr bool kEarlyLoad = D == 128;
+  if (kEarlyLoad && (kgrp ? 2 < nkv : true)) stg.load(X, (t0 + (kgrp ? 2 : 0)) * kBN, gtid);
   if (kgrp) __syncthreads();
   // Step 0 (no PV yet).
   {
     const int lt = kgrp ? 2 : 0;
-    if (lt < nkv) stg.load(X, (t0 + lt) * kBN, gtid);
+    if (!kEarlyLoad && lt < nkv) stg.load(X, (t0 + lt) * kBN, gtid);
     if (w_lo == 0 && w_end > 0) mphase(vbuf, kbuf, BoolC<false>{}, BoolC<true>{});
     __syncthreads();
     if (w_lo == 0 && w_end > 0) softmax(t0 * kBN);
     if (lt < nkv) stg.store(kgrp ? kbuf : vbuf, soff, sstride);
+    if (kEarlyLoad && lt + 1 < nkv) stg.load(X, (t0 + lt + 1) * kBN, gtid);
     __syncthreads();
   }
   // Steps 1 .. nkv-1, one code path. At step w_lo (a wave whose first
@@ -684,13 +693,14 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a) {
   // w_end (a wave past its last visible tile) the QK half is unused.
   for (int i = 1; i < nkv; ++i) {
     const int lt = kgrp ? i + 2 : i;  // the tile this group streams
-    if (lt < nkv) stg.load(X, (t0 + lt) * kBN, gtid);
+    if (!kEarlyLoad && lt < nkv) stg.load(X, (t0 + lt) * kBN, gtid);
     if (w_lo <= i && i <= w_end)
       mphase(vbuf + ((i - 1) & 1) * S::V_BYTES, kbuf + (i & 1) * S::K_BYTES, BoolC<true>{},
              BoolC<true>{});
     __syncthreads();
     if (w_lo <= i && i < w_end) softmax((t0 + i) * kBN);
     if (lt < nkv) stg.store(kgrp ? kbuf + (i & 1) * S::K_BYTES : vbuf + (i & 1) * S::V_BYTES, soff, sstride);
+    if (kEarlyLoad && lt + 1 < nkv) stg.load(X, (t0 + lt + 1) * kBN, gtid);
     __syncthreads();
   }
   // Final matrix phase: PV of the last tile.
