@@ -695,6 +695,11 @@ __device__ __forceinline__ void kv16_role(const BwdArgs& a, char* lds) {
         }
         pf[2 * qb + u] = Raw{w[0], w[1], w[2], w[3]};
       }
+    // Computed here, in the vector phase: otherwise the compiler sinks this
+    // work past the barrier to its first use, the next matrix phase, where
+    // it delays the MFMAs (about 110 VALU instructions per step).
+#pragma unroll
+    for (int p = 0; p < S::NP; ++p) settle(pf[p]);
   };
 
   // Prologue: stages 0 and 1 in LDS.
