@@ -558,7 +558,12 @@ __device__ __forceinline__ void kv16_role(const BwdArgs& a, char* lds) {
   asm volatile("" : "+s"(ts_off), "+s"(ta_off), "+s"(stat_off));
   const int rtid = tid & 255;
   u32x4 sx[S::NLD];
+  // The row statistic as loaded (clamped row), and whether the row is real.
+  // The scaling and the past-N select happen at the store, in the vector
+  // phase: applied at the load they made the loading wave wait for the
+  // global load inside its matrix phase.
   float stat = 0.f;
+  bool stat_ok = false;
   auto load = [&](int j) {
     const int q0 = step_q0(j);
     const size_t qh = (size_t)(bq0 + j / ns) * N;  // query head of the step
@@ -570,7 +575,8 @@ __device__ __forceinline__ void kv16_role(const BwdArgs& a, char* lds) {
     }
     if (rtid < kStepQ) {
       const int row = q0 + rtid;
-      stat = roleA ? (row < N ? a.lse[qh + row] * kLog2e : INFINITY) : (row < N ? a.dsum[qh + row] : 0.f);
+      stat = (roleA ? a.lse : a.dsum)[qh + min(row, N - 1)];
+      stat_ok = row < N;
     }
   };
   auto store = [&](auto kc) {  // into stage buffer kc
@@ -581,7 +587,7 @@ __device__ __forceinline__ void kv16_role(const BwdArgs& a, char* lds) {
       st<u32x4>(stage + tile_off<ROWB>(row, u * 16), sx[i]);
     }
     if (rtid < kStepQ)
-      st<float>(lds + stat_off + decltype(kc)::value * (kStepQ * 4) + rtid * 4, stat);
+      st<float>(lds + stat_off + decltype(kc)::value * (kStepQ * 4) + rtid * 4, roleA ? (stat_ok ? stat * kLog2e : INFINITY) : (stat_ok ? stat : 0.f));
   };
   auto stats_at = [&](auto kc) -> const char* { return lds + stat_off + decltype(kc)::value * (kStepQ * 4); };
   char* const px = lds + S::OFF_PX + slice * 4096 + lane * 16;  // this lane's P slots
