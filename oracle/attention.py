@@ -19,7 +19,7 @@ Sources (the pages this restates in code; cited by key below):
                  and an embedded answer "写一个flashattention算子" whose numbered
                  steps give the online-softmax update formulas.
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
   * scale: the scores are multiplied by ``scale`` (1/sqrt(d) in every
     workload, as in the answer's step 3, which divides by sqrt(d)); the
     softmax runs over the scaled scores.
@@ -33,8 +33,8 @@ Readings taken where the pages are silent (each also listed in the design doc):
     the definition (chain rule through softmax), written out below.
   * in the blockwise recurrence, a row that sees no key inside one block
     contributes nothing from that block (its block max is -inf, its block sum 0).
-  * local window (the block-sparse / sliding-window variant the survey
-    ranks next; the pages only show the causal special case): key j is
+  * local window (a sliding-window generalization of the causal block
+    skipping; the pages only show the causal special case): key j is
     visible to query i when i - left <= j <= i + right, a negative bound
     meaning unbounded on that side; combined with the causal rule when both
     are given. Causal is the window (unbounded, 0).
