@@ -38,6 +38,12 @@ Readings taken where the pages are silent:
     visible to query i when i - left <= j <= i + right, a negative bound
     meaning unbounded on that side; combined with the causal rule when both
     are given. Causal is the window (unbounded, 0).
+  * block-sparse attention (named with the window extension among the
+    method's sparse variants): a mask of blocks of mask_block query rows x
+    mask_block keys, shared by all batches and heads; a hidden block's
+    scores are excluded exactly. A row that then sees no key has O = 0 and
+    LSE = -inf (the softmax over an empty set has no value; these are its
+    limits as a single zero-valued key's score goes to -inf).
   * grouped K/V heads (multi-query / grouped-query attention, named next to
     the method on the pages' overview of later work): with Hq query heads
     and Hkv K/V heads (Hkv divides Hq), query head h attends with K/V head
@@ -66,15 +72,22 @@ def _f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def _visible(q_pos: np.ndarray, n_keys: int, causal: bool, window=None) -> np.ndarray | None:
+def _visible(q_pos: np.ndarray, n_keys: int, causal: bool, window=None,
+             block_mask=None, mask_block: int = 64) -> np.ndarray | None:
     """Boolean [rows, n_keys] mask of keys each query may attend to (None = all).
 
     Causal reading: query at absolute position i sees keys 0..i.
     Window (left, right): query i sees keys i-left .. i+right (negative = unbounded).
+    Block mask M (block-sparse attention): query i sees key j only if
+    M[i // mask_block, j // mask_block] is nonzero.
     """
     vis = None
+    if block_mask is not None:
+        bm = np.asarray(block_mask) != 0
+        vis = bm[q_pos[:, None] // mask_block, np.arange(n_keys)[None, :] // mask_block]
     if causal:
-        vis = np.arange(n_keys)[None, :] <= q_pos[:, None]
+        c = np.arange(n_keys)[None, :] <= q_pos[:, None]
+        vis = c if vis is None else vis & c
     if window is not None:
         left, right = window
         keys = np.arange(n_keys)[None, :]
@@ -118,7 +131,19 @@ def _scores(qc: np.ndarray, k: np.ndarray, scale: float, vis) -> np.ndarray:
     return s
 
 
-def _head_forward(q, k, v, scale, causal, q_pos, window=None):
+def _softmax_rows(s: np.ndarray):
+    """(P, LSE) of the rows of S (hidden entries -inf). A row with no visible
+    entry has P = 0 and LSE = -inf (the reading for an empty softmax)."""
+    m = s.max(axis=1, keepdims=True)                     # pass 1
+    m = np.where(np.isfinite(m), m, 0.0)
+    e = np.exp(s - m)
+    l = e.sum(axis=1, keepdims=True)                     # pass 2
+    p = np.where(l > 0, e / np.where(l > 0, l, 1.0), 0.0)  # pass 3
+    lse = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), -np.inf)
+    return p, lse[:, 0]
+
+
+def _head_forward(q, k, v, scale, causal, q_pos, window=None, block_mask=None, mask_block=64):
     """Three-pass safe softmax attention for one head.
 
     Pass 1: row max m of the scaled scores.     [FA-mem §2.2 safe softmax]
@@ -132,14 +157,17 @@ def _head_forward(q, k, v, scale, causal, q_pos, window=None):
     lse = np.empty(n_rows, dtype=np.float64)
     for r0 in range(0, n_rows, ROW_CHUNK):
         r1 = min(r0 + ROW_CHUNK, n_rows)
-        vis = _visible(q_pos[r0:r1], k.shape[0], causal, window)
+        vis = _visible(q_pos[r0:r1], k.shape[0], causal, window, block_mask, mask_block)
         s = _scores(q[r0:r1], k, scale, vis)
-        m = s.max(axis=1, keepdims=True)                 # pass 1
-        e = np.exp(s - m)
-        l = e.sum(axis=1, keepdims=True)                 # pass 2
-        p = e / l                                        # pass 3
+        if block_mask is None:
+            m = s.max(axis=1, keepdims=True)             # pass 1
+            e = np.exp(s - m)
+            l = e.sum(axis=1, keepdims=True)             # pass 2
+            p = e / l                                    # pass 3
+            lse[r0:r1] = (m + np.log(l))[:, 0]
+        else:  # rows may see no key at all
+            p, lse[r0:r1] = _softmax_rows(s)
         o[r0:r1] = p @ v
-        lse[r0:r1] = (m + np.log(l))[:, 0]
     return o, lse
 
 
@@ -155,7 +183,8 @@ def _batched(fn, arrays, n_out):
     return [np.stack(o).reshape(lead + o[0].shape) for o in outs]
 
 
-def attention_forward(q, k, v, scale: float, causal: bool, q_positions=None, window=None):
+def attention_forward(q, k, v, scale: float, causal: bool, q_positions=None, window=None,
+                      block_mask=None, mask_block: int = 64):
     """O = softmax(scale * Q K^T [masked]) V and the per-row LSE.
 
     Shapes: q [..., Hq, Nq, d], k [..., Hkv, Nk, d], v [..., Hkv, Nk, dv]
@@ -163,7 +192,11 @@ def attention_forward(q, k, v, scale: float, causal: bool, q_positions=None, win
     multi-head attention has Hkv = Hq). ``q_positions`` gives the absolute
     position of each query row for the causal and window masks (default
     0..Nq-1), which lets a caller evaluate a sampled subset of rows of a long
-    sequence exactly. ``window`` = (left, right) or None.
+    sequence exactly. ``window`` = (left, right) or None. ``block_mask``
+    (block-sparse attention): a [ceil(N/mask_block)]^2 array shared by all
+    batches and heads; query i sees key j only where
+    block_mask[i // mask_block, j // mask_block] is nonzero. With a block
+    mask a row may see no key: its O is 0 and its LSE -inf.
 
     Returns (O [..., Hq, Nq, dv], LSE [..., Hq, Nq]), float64.
     """
@@ -172,11 +205,13 @@ def attention_forward(q, k, v, scale: float, causal: bool, q_positions=None, win
     pos = np.arange(q.shape[-2]) if q_positions is None else np.asarray(q_positions)
     if pos.shape != (q.shape[-2],):
         raise ValueError("q_positions must have one entry per query row")
-    return tuple(_batched(lambda a, b, c: _head_forward(a, b, c, scale, causal, pos, window),
+    return tuple(_batched(lambda a, b, c: _head_forward(a, b, c, scale, causal, pos, window,
+                                                        block_mask, mask_block),
                           [q, k, v], 2))
 
 
-def attention_probabilities(q, k, scale: float, causal: bool, window=None, q_positions=None):
+def attention_probabilities(q, k, scale: float, causal: bool, window=None, q_positions=None,
+                            block_mask=None, mask_block: int = 64):
     """P = softmax(scale * Q K^T) materialized ([..., rows, N]; tests only).
     With ``q_positions``, q holds only those rows (their sequence positions)."""
     q, k = _f64(q), _f64(k)
@@ -184,14 +219,13 @@ def attention_probabilities(q, k, scale: float, causal: bool, window=None, q_pos
     pos = np.arange(q.shape[-2]) if q_positions is None else np.asarray(q_positions)
 
     def one(a, b):
-        s = _scores(a, b, scale, _visible(pos, b.shape[0], causal, window))
-        e = np.exp(s - s.max(axis=1, keepdims=True))
-        return (e / e.sum(axis=1, keepdims=True),)
+        s = _scores(a, b, scale, _visible(pos, b.shape[0], causal, window, block_mask, mask_block))
+        return (_softmax_rows(s)[0],)
 
     return _batched(one, [q, k], 1)[0]
 
 
-def _head_backward(q, k, v, do, scale, causal, window=None):
+def _head_backward(q, k, v, do, scale, causal, window=None, block_mask=None, mask_block=64):
     """Gradients of sum(dO * O) for one head, from the definition.
 
     Not on the pages (the answer's step 6 only says the scores are recomputed
@@ -211,9 +245,13 @@ def _head_backward(q, k, v, do, scale, causal, window=None):
     dsum = np.empty(n)
     for r0 in range(0, n, ROW_CHUNK):
         r1 = min(r0 + ROW_CHUNK, n)
-        s = _scores(q[r0:r1], k, scale, _visible(pos[r0:r1], k.shape[0], causal, window))
-        e = np.exp(s - s.max(axis=1, keepdims=True))
-        p = e / e.sum(axis=1, keepdims=True)
+        s = _scores(q[r0:r1], k, scale,
+                    _visible(pos[r0:r1], k.shape[0], causal, window, block_mask, mask_block))
+        if block_mask is None:
+            e = np.exp(s - s.max(axis=1, keepdims=True))
+            p = e / e.sum(axis=1, keepdims=True)
+        else:  # rows may see no key at all (P = 0 there)
+            p = _softmax_rows(s)[0]
         dv += p.T @ do[r0:r1]
         dp = do[r0:r1] @ v.T
         d_i = (p * dp).sum(axis=1, keepdims=True)
@@ -224,7 +262,8 @@ def _head_backward(q, k, v, do, scale, causal, window=None):
     return dq, dk, dv, dsum
 
 
-def attention_backward(q, k, v, do, scale: float, causal: bool, window=None):
+def attention_backward(q, k, v, do, scale: float, causal: bool, window=None, block_mask=None,
+                       mask_block: int = 64):
     """(dQ, dK, dV, D) for the loss sum(dO * O), all float64.
 
     D is the per-row term sum_j P_ij dP_ij (returned so tests can check that it
@@ -235,7 +274,8 @@ def attention_backward(q, k, v, do, scale: float, causal: bool, window=None):
     hkv = k.shape[-3] if k.ndim >= 3 else None
     k, v = _expand_kv(q, k, v)
     dq, dk, dv, dsum = _batched(
-        lambda a, b, c, g: _head_backward(a, b, c, g, scale, causal, window), [q, k, v, do], 4)
+        lambda a, b, c, g: _head_backward(a, b, c, g, scale, causal, window, block_mask,
+                                          mask_block), [q, k, v, do], 4)
     if hkv is not None:
         dk, dv = _reduce_kv_grad(dk, hkv), _reduce_kv_grad(dv, hkv)
     return dq, dk, dv, dsum

@@ -420,3 +420,104 @@ def test_grouped_window_matches_torch_float64_and_autograd(window, causal):
     np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-11)
     np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-11)
     np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-11)
+
+
+# ---------------------------------------------------------- block-sparse masks
+def brute_force_blocks(q, k, v, scale, causal, mask, mb):
+    """Pure-Python loops for one head with a block mask of mb x mb blocks; a
+    row with no visible key gets O = 0 and LSE = -inf."""
+    o, lse = [], []
+    for i in range(len(q)):
+        w = []
+        for j in range(len(k)):
+            vis = mask[i // mb][j // mb] != 0 and not (causal and j > i)
+            w.append(math.exp(scale * sum(a * b for a, b in zip(q[i], k[j]))) if vis else 0.0)
+        z = sum(w)
+        lse.append(math.log(z) if z > 0 else -math.inf)
+        o.append([sum(w[j] * v[j][c] for j in range(len(k))) / z if z > 0 else 0.0
+                  for c in range(len(v[0]))])
+    return np.array(o), np.array(lse)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n,mb", [(7, 2), (9, 3), (12, 4)])
+def test_block_mask_brute_force(causal, n, mb):
+    nb = -(-n // mb)
+    mask = np.random.default_rng(n + mb).integers(0, 2, size=(nb, nb)).astype(np.uint8)
+    mask[1, :] = 0  # a block row that sees nothing
+    mask[0, 0] = 1
+    q, k, v = rand((n, 3), n), rand((n, 3), n + 1), rand((n, 2), n + 2)
+    o, lse = attention_forward(q, k, v, 0.7, causal, block_mask=mask, mask_block=mb)
+    bo, blse = brute_force_blocks(q.tolist(), k.tolist(), v.tolist(), 0.7, causal, mask.tolist(), mb)
+    np.testing.assert_allclose(o, bo, rtol=0, atol=1e-12)
+    fin = np.isfinite(blse)
+    assert np.array_equal(np.isfinite(lse), fin) and (~fin).any()
+    np.testing.assert_allclose(lse[fin], blse[fin], rtol=0, atol=1e-12)
+    assert (o[~fin] == 0).all()
+    p = attention_probabilities(q, k, 0.7, causal, block_mask=mask, mask_block=mb)
+    np.testing.assert_allclose(p.sum(axis=-1), fin.astype(float), rtol=0, atol=1e-12)
+
+
+def test_all_ones_block_mask_equals_dense():
+    q, k, v = rand((2, 3, 70, 8), 1), rand((2, 3, 70, 8), 2), rand((2, 3, 70, 8), 3)
+    ones = np.ones((2, 2), dtype=np.uint8)
+    for causal in (False, True):
+        o0, l0 = attention_forward(q, k, v, 0.3, causal)
+        o1, l1 = attention_forward(q, k, v, 0.3, causal, block_mask=ones)
+        np.testing.assert_allclose(o1, o0, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(l1, l0, rtol=0, atol=1e-13)
+
+
+def test_block_diagonal_mask_is_attention_within_each_block():
+    """Closed form: with only diagonal blocks visible, each block of rows is
+    ordinary attention over its own keys."""
+    n, mb = 12, 4
+    q, k, v = rand((n, 5), 4), rand((n, 5), 5), rand((n, 3), 6)
+    mask = np.eye(3, dtype=np.uint8)
+    for causal in (False, True):
+        o, lse = attention_forward(q, k, v, 0.9, causal, block_mask=mask, mask_block=mb)
+        for b in range(3):
+            sl = slice(mb * b, mb * b + mb)
+            ob, lb = attention_forward(q[sl], k[sl], v[sl], 0.9, causal)
+            np.testing.assert_allclose(o[sl], ob, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse[sl], lb, rtol=0, atol=1e-12)
+
+
+def test_hidden_blocks_do_not_matter():
+    """Changing K and V inside blocks no row sees changes nothing."""
+    n, mb = 16, 4
+    q, k, v = rand((n, 4), 7), rand((n, 4), 8), rand((n, 4), 9)
+    mask = np.ones((4, 4), dtype=np.uint8)
+    mask[:, 2] = 0  # key block 2 hidden from every row
+    k2, v2 = k.copy(), v.copy()
+    k2[8:12] += 5.0
+    v2[8:12] -= 3.0
+    o1, l1 = attention_forward(q, k, v, 1.1, False, block_mask=mask, mask_block=mb)
+    o2, l2 = attention_forward(q, k2, v2, 1.1, False, block_mask=mask, mask_block=mb)
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l2, l1, rtol=0, atol=1e-13)
+
+
+def test_block_mask_gradients_match_finite_differences():
+    n, mb = 10, 3
+    q, k, v, do = rand((n, 3), 21), rand((n, 3), 22), rand((n, 2), 23), rand((n, 2), 24)
+    mask = np.array([[1, 0, 1, 0], [1, 1, 0, 0], [0, 1, 1, 0], [1, 0, 0, 1]], dtype=np.uint8)
+    mask[1, :] = 0  # rows 3..5 see nothing: zero gradients through them
+    dq, dk, dv, _ = attention_backward(q, k, v, do, 0.8, True, block_mask=mask, mask_block=mb)
+    assert (dq[3:6] == 0).all()
+    h = 1e-6
+
+    def loss(qq, kk, vv):
+        o, _ = attention_forward(qq, kk, vv, 0.8, True, block_mask=mask, mask_block=mb)
+        return float((o * do).sum())
+
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+            args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8, err_msg=name)

@@ -34,8 +34,17 @@ MUTATIONS = [
      "return np.tile(k, (group, 1, 1)), np.tile(v, (group, 1, 1))"),
     ("grouped K/V gradient averaged instead of summed",
      "+ g.shape[-2:]).sum(axis=-3)", "+ g.shape[-2:]).mean(axis=-3)"),
-    ("max over the wrong axis", "m = s.max(axis=1, keepdims=True)",
-     "m = s.max(axis=0, keepdims=True)"),
+    ("max over the wrong axis", "m = s.max(axis=1, keepdims=True)             # pass 1",
+     "m = s.max(axis=0, keepdims=True)             # pass 1"),
+    ("block mask transposed",
+     "vis = bm[q_pos[:, None] // mask_block, np.arange(n_keys)[None, :] // mask_block]",
+     "vis = bm[np.arange(n_keys)[None, :] // mask_block, q_pos[:, None] // mask_block]"),
+    ("block mask replaces the causal rule", "vis = c if vis is None else vis & c",
+     "vis = c if vis is None else vis"),
+    ("empty rows get LSE 0", "lse = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), -np.inf)",
+     "lse = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), 0.0)"),
+    ("empty rows keep a uniform P", "p = np.where(l > 0, e / np.where(l > 0, l, 1.0), 0.0)",
+     "p = np.where(l > 0, e / np.where(l > 0, l, 1.0), 1.0 / s.shape[1])"),
     ("LSE without the max", "lse[r0:r1] = (m + np.log(l))[:, 0]",
      "lse[r0:r1] = (np.log(l))[:, 0]"),
     ("LSE without the log", "lse[r0:r1] = (m + np.log(l))[:, 0]",
@@ -87,6 +96,12 @@ PINS = [
     (T.test_grouped_heads_equal_repeated_heads_and_mqa_closed_form, {}),
     (T.test_window_gradients_match_finite_differences, dict(window=(2, 1))),
     (T.test_grouped_window_matches_torch_float64_and_autograd, dict(window=(5, 3), causal=False)),
+    (T.test_block_mask_brute_force, dict(causal=True, n=7, mb=2)),
+    (T.test_block_mask_brute_force, dict(causal=False, n=12, mb=4)),
+    (T.test_all_ones_block_mask_equals_dense, {}),
+    (T.test_block_diagonal_mask_is_attention_within_each_block, {}),
+    (T.test_hidden_blocks_do_not_matter, {}),
+    (T.test_block_mask_gradients_match_finite_differences, {}),
 ]
 
 
