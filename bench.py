@@ -239,8 +239,8 @@ def run_variants(args):
     """Time the variant rows against the plain calls (HIP events on the
     current stream, back-to-back calls with preallocated buffers): split-KV
     on short/few-head shapes, grouped K/V heads and a local window at
-    N = 16384, and the E4M3 forward against the bf16 one. One JSON line per
-    case."""
+    N = 16384, block-sparse masks at N = 16384, and the E4M3 forward against
+    the bf16 one. One JSON line per case."""
     import torch
 
     import exact_attention_120_amd as fa
@@ -310,6 +310,42 @@ def run_variants(args):
                           "causal": causal, "window": window, "fwd_ms": f_ms, "bwd_ms": b_ms,
                           "fwd_tflops": fl / (f_ms * 1e-3) / 1e12,
                           "bwd_tflops": 2.5 * fl / (b_ms * 1e-3) / 1e12}), flush=True)
+
+    # Block-sparse masks (64 x 64 blocks) at B=1 H=16 N=16384 d=128, forward
+    # and backward, against the dense calls. FLOP counts the visible
+    # (query, key) pairs only; "dense" is the all-ones mask (the sparse
+    # kernels' overhead over the plain ones).
+    from fa_inputs import make_block_mask
+    inp = make_inputs(B, H, N, d, "bf16", seed=0, backward=True)
+    q, k, v, do = (inp[x].to(dev) for x in ("q", "k", "v", "do"))
+    o, lse = torch.empty_like(q), torch.empty((B, H, N), device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device=dev)
+    for causal in (False, True):
+        f_dense = per_call_ms(lambda: fa.fa_fwd(q, k, v, o, lse, sc, causal))
+        b_dense = per_call_ms(lambda: fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, sc, causal, ws))
+        for kind, dens in (("dense", 1.0), ("random", 0.5), ("random", 0.25),
+                           ("band_global", 0.05)):
+            m = make_block_mask(N, kind, seed=0, density=dens)
+            ib, jb = torch.meshgrid(torch.arange(m.shape[0]), torch.arange(m.shape[0]),
+                                    indexing="ij")
+            per_block = (torch.where(jb < ib, 4096.0, torch.where(jb == ib, 2080.0, 0.0))
+                         if causal else torch.full(m.shape, 4096.0))
+            pairs = float((per_block * (m != 0)).sum())
+            fl = 4.0 * B * H * pairs * d
+            md = m.to(dev)
+            f_ms = per_call_ms(lambda: fa.fa_fwd_sparse(q, k, v, o, lse, sc, causal, md))
+            b_ms = per_call_ms(lambda: fa.fa_bwd_sparse(q, k, v, o, do, lse, dq, dk, dv, sc,
+                                                        causal, md, ws))
+            print(json.dumps({"case": "block_sparse", "B": B, "H": H, "N": N, "d": d,
+                              "causal": causal, "mask": kind, "density": dens,
+                              "kept_blocks": float((m != 0).float().mean()),
+                              "fwd_ms": f_ms, "bwd_ms": b_ms,
+                              "dense_fwd_ms": f_dense, "dense_bwd_ms": b_dense,
+                              "fwd_tflops": fl / (f_ms * 1e-3) / 1e12,
+                              "bwd_tflops": 2.5 * fl / (b_ms * 1e-3) / 1e12,
+                              "fwd_speedup_vs_dense": f_dense / f_ms,
+                              "bwd_speedup_vs_dense": b_dense / b_ms}), flush=True)
 
     # 8-bit float forward (E4M3 Q, K, V, bf16 O) against the bf16 forward on
     # the same shape. Peak: MI355X dense FP8 MFMA, 5.0 PFLOP/s.
@@ -389,10 +425,17 @@ def _short(name: str) -> str:
                 f"{'causal' if 'Lb1' in a else 'noncausal'},out="
                 f"{'bf16' if 'DF16b' in a else 'f16'}>")
     if m:
-        args = m.group(2).replace("DF16b", "bf16,").replace("DF16_", "f16,").replace("f", "f32,", 1)\
-            if m.group(2).startswith("f") else m.group(2).replace("DF16b", "bf16,").replace("DF16_", "f16,")
-        args = args.replace("Li", "d=").replace("ELb0", ",noncausal").replace("ELb1", ",causal")
-        return m.group(1) + "<" + args.rstrip("E").rstrip(",") + ">"
+        a = m.group(2)
+        ty = "bf16" if a.startswith("DF16b") else "f16" if a.startswith("DF16_") else \
+            "f32" if a.startswith("f") else ""
+        d = re.search(r"Li(\d+)E", a)
+        flags = re.findall(r"Lb([01])E", a)
+        parts = [ty] + ([f"d={d.group(1)}"] if d else [])
+        if flags:
+            parts.append("causal" if flags[0] == "1" else "noncausal")
+        if len(flags) > 1 and flags[1] == "1":
+            parts.append("sparse")
+        return m.group(1) + "<" + ",".join(p for p in parts if p) + ">"
     return name[:70]
 
 

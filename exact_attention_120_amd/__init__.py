@@ -12,6 +12,9 @@ Grouped K/V heads are expressed by the shape of k and v ([B, Hkv, N, d] with
 Hkv dividing H); a local window by ``window=(left, right)`` where a negative
 (or None) bound is unbounded on that side. ``fa_fwd_fp8``/``forward_fp8``
 take Q, K, V as OCP FP8 E4M3 codes with one dequantization factor each.
+``fa_fwd_sparse``/``fa_bwd_sparse`` (and ``block_mask=`` of ``forward`` and
+``backward``) take a [ceil(N/64)]^2 byte map of the (64-row query block,
+64-key block) pairs whose scores are kept.
 """
 
 from __future__ import annotations
@@ -25,8 +28,8 @@ from . import _lib
 
 __all__ = ["FaError", "fa_fwd", "fa_bwd", "fa_fwd_ex", "fa_bwd_ex", "fa_bwd_workspace_size",
            "fa_fwd_num_splits", "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv",
-           "fa_fwd_fp8", "fa_strerror", "forward", "forward_fp8", "backward", "DTYPES",
-           "FP8_DTYPES"]
+           "fa_fwd_fp8", "fa_fwd_sparse", "fa_bwd_sparse", "fa_strerror", "forward",
+           "forward_fp8", "backward", "DTYPES", "FP8_DTYPES", "MASK_BLOCK"]
 
 DTYPES = {torch.float32: _lib.FA_F32, torch.float16: _lib.FA_F16,
           torch.bfloat16: _lib.FA_BF16}
@@ -222,6 +225,59 @@ def fa_fwd_fp8(q8, k8, v8, o, lse, scale: float, causal: bool, q_descale: float,
         raise FaError(st, "fa_fwd_fp8")
 
 
+MASK_BLOCK = _lib.FA_MASK_BLOCK
+
+
+def _check_mask(mask, N: int, device) -> None:
+    nmb = (N + MASK_BLOCK - 1) // MASK_BLOCK
+    if not mask.is_cuda or mask.device != device or mask.dtype not in (torch.uint8, torch.bool) \
+            or tuple(mask.shape) != (nmb, nmb) or not mask.is_contiguous():
+        raise ValueError(f"block_mask: expected a contiguous ({nmb}, {nmb}) uint8/bool tensor on "
+                         f"{device}, got {tuple(mask.shape)} {mask.dtype} on {mask.device}")
+
+
+def fa_fwd_sparse(q, k, v, o, lse, scale: float, causal: bool, block_mask, window=None,
+                  stream=None) -> None:
+    """fa_fwd_ex under a block mask: ``block_mask`` is a [ceil(N/64)]^2 uint8
+    (or bool) GPU tensor; query block i sees key block j where it is nonzero."""
+    B, H, Hkv, N, d = _kv_shape(q, k)
+    _check({"q": q, "o": o}, (B, H, N, d), q.dtype)
+    _check({"k": k, "v": v}, (B, Hkv, N, d), q.dtype)
+    _check({"lse": lse}, (B, H, N), torch.float32)
+    _check_mask(block_mask, N, q.device)
+    opts = _options(Hkv, window)
+    with torch.cuda.device(q.device):
+        st = _lib.load().fa_fwd_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                       lse.data_ptr(), B, H, N, d, float(scale),
+                                       int(bool(causal)), DTYPES[q.dtype], ctypes.byref(opts),
+                                       block_mask.data_ptr(), _stream(q, stream))
+    if st != _lib.FA_OK:
+        raise FaError(st, "fa_fwd_sparse")
+
+
+def fa_bwd_sparse(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool, block_mask,
+                  workspace, window=None, stream=None) -> None:
+    """fa_bwd_ex under the forward's block mask."""
+    B, H, Hkv, N, d = _kv_shape(q, k)
+    _check({"q": q, "o": o, "do": do, "dq": dq}, (B, H, N, d), q.dtype)
+    _check({"k": k, "v": v, "dk": dk, "dv": dv}, (B, Hkv, N, d), q.dtype)
+    _check({"lse": lse}, (B, H, N), torch.float32)
+    _check_mask(block_mask, N, q.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    opts = _options(Hkv, window)
+    with torch.cuda.device(q.device):
+        st = _lib.load().fa_bwd_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                       do.data_ptr(), lse.data_ptr(), dq.data_ptr(),
+                                       dk.data_ptr(), dv.data_ptr(), B, H, N, d, float(scale),
+                                       int(bool(causal)), DTYPES[q.dtype], ctypes.byref(opts),
+                                       block_mask.data_ptr(), workspace.data_ptr(),
+                                       workspace.numel() * workspace.element_size(),
+                                       _stream(q, stream))
+    if st != _lib.FA_OK:
+        raise FaError(st, "fa_bwd_sparse")
+
+
 def forward_fp8(q8, k8, v8, descale=(1.0, 1.0, 1.0), causal: bool = False,
                 scale: float | None = None, out_dtype=torch.bfloat16, window=None, stream=None):
     """Allocate O (``out_dtype``) and LSE with torch and run fa_fwd_fp8;
@@ -243,14 +299,20 @@ def _default_scale(d: int, scale):
 
 
 def forward(q, k, v, causal: bool = False, scale: float | None = None, stream=None,
-            window=None, num_splits: int | None = None):
+            window=None, num_splits: int | None = None, block_mask=None):
     """Allocate O and LSE with torch and run fa_fwd (fa_fwd_ex when k, v have
     fewer heads than q or a window is given; fa_fwd_splitkv, with a workspace
-    allocated here, when ``num_splits`` is given); returns (o, lse)."""
+    allocated here, when ``num_splits`` is given; fa_fwd_sparse when
+    ``block_mask`` is given); returns (o, lse)."""
     B, H, N, d = _shape(q)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if num_splits is not None:
+    if block_mask is not None:
+        if num_splits is not None:
+            raise ValueError("block_mask and num_splits cannot be combined")
+        fa_fwd_sparse(q, k, v, o, lse, _default_scale(d, scale), causal, block_mask, window,
+                      stream)
+    elif num_splits is not None:
         nbytes = fa_fwd_splitkv_workspace_size(B, H, N, d, q.dtype, num_splits)
         ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
         fa_fwd_splitkv(q, k, v, o, lse, _default_scale(d, scale), causal, num_splits, ws,
@@ -263,15 +325,19 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, stream=No
 
 
 def backward(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None,
-             stream=None, workspace=None, window=None):
+             stream=None, workspace=None, window=None, block_mask=None):
     """Allocate dQ, dK, dV (and the workspace unless given) and run fa_bwd
-    (fa_bwd_ex when k, v have fewer heads than q or a window is given)."""
+    (fa_bwd_ex when k, v have fewer heads than q or a window is given,
+    fa_bwd_sparse when ``block_mask`` is given)."""
     B, H, N, d = _shape(q)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if workspace is None:
         workspace = torch.empty(fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8,
                                 device=q.device)
-    if _plain(q, k, window):
+    if block_mask is not None:
+        fa_bwd_sparse(q, k, v, o, do, lse, dq, dk, dv, _default_scale(d, scale), causal,
+                      block_mask, workspace, window, stream)
+    elif _plain(q, k, window):
         fa_bwd(q, k, v, o, do, lse, dq, dk, dv, _default_scale(d, scale), causal, workspace,
                stream)
     else:

@@ -12,6 +12,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "fa.h")
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_OK = 0
+FA_MASK_BLOCK = 64
 
 _c = ctypes
 _vp, _int, _flt, _sz = _c.c_void_p, _c.c_int, _c.c_float, _c.c_size_t
@@ -40,6 +41,10 @@ SIGNATURES = {
                               _opt, _int, _vp, _sz, _vp]),
     "fa_fwd_fp8": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _flt, _int, _flt, _flt,
                           _flt, _int, _opt, _vp]),
+    "fa_fwd_sparse": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _flt, _int, _int,
+                             _opt, _vp, _vp]),
+    "fa_bwd_sparse": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int,
+                             _flt, _int, _int, _opt, _vp, _vp, _sz, _vp]),
     "fa_strerror": (_c.c_char_p, [_int]),
 }
 

@@ -68,13 +68,19 @@ int read_opts(const fa_options* o, int H, Opts* out) {
   return FA_OK;
 }
 
-}  // namespace
+// Block-sparse calls: the mask's side in blocks (N <= 65536, 16-bit types),
+// or the status to report (as a negative number).
+int mask_blocks(const void* mask, int N, int dtype) {
+  if (!mask) return FA_ERR_INVALID_ARG;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  const int nmb = (N + fa::kMaskBlock - 1) / fa::kMaskBlock;
+  if (nmb > fa::kMaxMaskBlocks) return FA_ERR_UNSUPPORTED;
+  return nmb;
+}
 
-extern "C" {
-
-int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-              int N, int d, float scale, int causal, int dtype, const fa_options* opts,
-              void* stream) {
+int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+             int N, int d, float scale, int causal, int dtype, const fa_options* opts,
+             const void* mask, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   int st = check_shape(B, H, N, d, scale, causal, dtype);
   if (st != FA_OK) return st;
@@ -93,7 +99,80 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, 
 
   fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, exp2_scale(scale), causal, dtype,
                 op.Hkv, op.wl, op.wr};
+  if (mask) {
+    const int nmb = mask_blocks(mask, N, dtype);
+    if (nmb < 0) return nmb;
+    const size_t mb = (size_t)nmb * nmb;
+    if (overlap(mask, mb, o, tb) || overlap(mask, mb, lse, lb)) return FA_ERR_INVALID_ARG;
+    a.block_mask = static_cast<const uint8_t*>(mask);
+    a.nmb = nmb;
+  }
   return hip_status(fa::launch_fwd(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dO,
+             const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+             float scale, int causal, int dtype, const fa_options* opts, const void* mask,
+             void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv || !workspace)
+    return FA_ERR_INVALID_ARG;
+  int st = check_shape(B, H, N, d, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  Opts op;
+  if ((st = read_opts(opts, H, &op)) != FA_OK) return st;
+  const void* ptrs[] = {q, k, v, o, dO, lse, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return FA_ERR_ALIGN;
+  const size_t need = fa_bwd_workspace_size(B, H, N, d);
+  if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+
+  const size_t tb = (size_t)B * H * N * d * elem_size(dtype);
+  const size_t kb = (size_t)B * op.Hkv * N * d * elem_size(dtype);
+  const size_t lb = (size_t)B * H * N * sizeof(float);
+  struct Range { const void* p; size_t n; };
+  const Range ins[] = {{q, tb}, {k, kb}, {v, kb}, {o, tb}, {dO, tb}, {lse, lb}};
+  const Range outs[] = {{dq, tb}, {dk, kb}, {dv, kb}, {workspace, need}};
+  for (const Range& w : outs) {
+    for (const Range& r : ins)
+      if (overlap(w.p, w.n, r.p, r.n)) return FA_ERR_INVALID_ARG;
+    for (const Range& x : outs)
+      if (&x != &w && overlap(w.p, w.n, x.p, x.n)) return FA_ERR_INVALID_ARG;
+  }
+
+  char* ws = static_cast<char*>(workspace);
+  float* dsum = reinterpret_cast<float*>(ws);
+  float* scratch = reinterpret_cast<float*>(ws + round_up(lb));
+  fa::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, dsum, scratch,
+                B, H, N, d, scale, exp2_scale(scale), causal, dtype, op.Hkv, op.wl, op.wr,
+                scratch};
+  if (mask) {
+    const int nmb = mask_blocks(mask, N, dtype);
+    if (nmb < 0) return nmb;
+    const size_t mb = (size_t)nmb * nmb;
+    for (const Range& w : outs)
+      if (overlap(mask, mb, w.p, w.n)) return FA_ERR_INVALID_ARG;
+    a.block_mask = static_cast<const uint8_t*>(mask);
+    a.nmb = nmb;
+  }
+  return hip_status(fa::launch_bwd(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+              int N, int d, float scale, int causal, int dtype, const fa_options* opts,
+              void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, opts, nullptr, stream);
+}
+
+int fa_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                  int H, int N, int d, float scale, int causal, int dtype,
+                  const fa_options* opts, const void* block_mask, void* stream) {
+  if (!block_mask) return FA_ERR_INVALID_ARG;
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, opts, block_mask, stream);
 }
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -202,39 +281,18 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
               const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
               float scale, int causal, int dtype, const fa_options* opts, void* workspace,
               size_t workspace_bytes, void* stream) {
-  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv || !workspace)
-    return FA_ERR_INVALID_ARG;
-  int st = check_shape(B, H, N, d, scale, causal, dtype);
-  if (st != FA_OK) return st;
-  Opts op;
-  if ((st = read_opts(opts, H, &op)) != FA_OK) return st;
-  const void* ptrs[] = {q, k, v, o, dO, lse, dq, dk, dv};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return FA_ERR_ALIGN;
-  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return FA_ERR_ALIGN;
-  const size_t need = fa_bwd_workspace_size(B, H, N, d);
-  if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+  return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, opts,
+                  nullptr, workspace, workspace_bytes, stream);
+}
 
-  const size_t tb = (size_t)B * H * N * d * elem_size(dtype);
-  const size_t kb = (size_t)B * op.Hkv * N * d * elem_size(dtype);
-  const size_t lb = (size_t)B * H * N * sizeof(float);
-  struct Range { const void* p; size_t n; };
-  const Range ins[] = {{q, tb}, {k, kb}, {v, kb}, {o, tb}, {dO, tb}, {lse, lb}};
-  const Range outs[] = {{dq, tb}, {dk, kb}, {dv, kb}, {workspace, need}};
-  for (const Range& w : outs) {
-    for (const Range& r : ins)
-      if (overlap(w.p, w.n, r.p, r.n)) return FA_ERR_INVALID_ARG;
-    for (const Range& x : outs)
-      if (&x != &w && overlap(w.p, w.n, x.p, x.n)) return FA_ERR_INVALID_ARG;
-  }
-
-  char* ws = static_cast<char*>(workspace);
-  float* dsum = reinterpret_cast<float*>(ws);
-  float* scratch = reinterpret_cast<float*>(ws + round_up(lb));
-  fa::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, dsum, scratch,
-                B, H, N, d, scale, exp2_scale(scale), causal, dtype, op.Hkv, op.wl, op.wr,
-                scratch};
-  return hip_status(fa::launch_bwd(a, reinterpret_cast<hipStream_t>(stream)));
+int fa_bwd_sparse(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                  const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                  float scale, int causal, int dtype, const fa_options* opts,
+                  const void* block_mask, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  if (!block_mask) return FA_ERR_INVALID_ARG;
+  return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, opts,
+                  block_mask, workspace, workspace_bytes, stream);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,

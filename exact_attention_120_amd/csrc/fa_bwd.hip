@@ -461,6 +461,9 @@ struct KVShape {
   static constexpr int REG_DSUM = REG_LSE + NSTAGE * kStepQ * 4;
   static constexpr int OFF_PX = REG_DSUM + NSTAGE * kStepQ * 4;  // P exchange: 4 slices x 4 KB
   static constexpr int LDS = OFF_PX + 4 * 4096;
+  // Block-sparse: the list of query blocks and the compaction scratch.
+  static constexpr int OFF_TL = LDS;
+  static constexpr int LDS_SPARSE = OFF_TL + 2 * kMaxMaskBlocks + 4 * 8;
   static constexpr int UNITS = D / 8;
   static constexpr int NLD = kStepQ * UNITS / 256;    // loads per thread (one tensor, one role)
   static constexpr int NQK = D / 16;
@@ -480,7 +483,7 @@ struct IntC {
 // loop-invariant per-lane base plus an immediate offset: with a runtime
 // stage index the matrix phase re-added the stage and role offsets to each
 // of its address registers (about as many VALU instructions as MFMAs).
-template <typename T, int D, bool CAUSAL, bool ROLE_A>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool ROLE_A>
 __device__ __forceinline__ void kv16_role(const BwdArgs& a, char* lds) {
   using S = KVShape<D>;
   using E = Elem<T>;
@@ -529,11 +532,31 @@ __device__ __forceinline__ void kv16_role(const BwdArgs& a, char* lds) {
   for (int i = 0; i < S::NQK; ++i) aoff[i] = tile_off<ROWB>(col, (half * (D / 2) + 8 * i) * 2);
 
   // Query steps [it0, it0 + ns) hold every row that sees a key of the tile;
-  // step j covers query head j / ns, step it0 + j % ns.
+  // step j covers query head j / ns, step it0 + j % ns. Block-sparse: the
+  // steps are the query blocks of that range that keep one of the
+  // workgroup's two 64-key blocks (an LDS list, entries flagging which); a
+  // wave whose key block a step's block drops hides all its scores there.
   const int it0 = first_query_seeing(k0, CAUSAL, a.wr) / kStepQ;
-  const int ns = last_query_seeing(min(k0 + kBN, N) - 1, N, a.wl) / kStepQ - it0 + 1;
+  int ns = last_query_seeing(min(k0 + kBN, N) - 1, N, a.wl) / kStepQ - it0 + 1;
+  const uint16_t* qlist = nullptr;
+  if constexpr (SPARSE) {
+    uint16_t* sl = reinterpret_cast<uint16_t*>(lds + S::OFF_TL);
+    int* sw = reinterpret_cast<int*>(lds + S::OFF_TL + 2 * kMaxMaskBlocks);
+    const int kb0 = k0 / kMaskBlock;
+    const int nxb = min(kBN / kMaskBlock, a.nmb - kb0);
+    ns = compact_blocks<kKVThreads, 2>(a.block_mask, (long long)it0 * a.nmb + kb0, a.nmb, 1, nxb,
+                                       ns, sl, sw);
+    qlist = sl;
+  }
   const int nsteps = grp * ns;
-  auto step_q0 = [&](int j) { return (it0 + j % ns) * kStepQ; };
+  auto step_q0 = [&](int j) -> int {
+    if constexpr (SPARSE) return (it0 + (__builtin_amdgcn_readfirstlane(qlist[j % ns]) >> 2)) * kStepQ;
+    return (it0 + j % ns) * kStepQ;
+  };
+  auto kept = [&](int j) -> bool {
+    if constexpr (SPARSE) return (__builtin_amdgcn_readfirstlane(qlist[j % ns]) >> (slice >> 1)) & 1;
+    return true;
+  };
   const float c = a.scale_log2;
 
   f32x16 acc[S::NDT];  // role A: dV^T, role B: dK^T (rows = head dim, lane = key)
@@ -587,7 +610,9 @@ __device__ __forceinline__ void kv16_role(const BwdArgs& a, char* lds) {
       st<u32x4>(stage + tile_off<ROWB>(row, u * 16), sx[i]);
     }
     if (rtid < kStepQ)
-      st<float>(lds + stat_off + decltype(kc)::value * (kStepQ * 4) + rtid * 4, roleA ? (stat_ok ? stat * kLog2e : INFINITY) : (stat_ok ? stat : 0.f));
+      // (A row whose LSE is -inf -- it sees no key -- gets +inf: P = 0.)
+      st<float>(lds + stat_off + decltype(kc)::value * (kStepQ * 4) + rtid * 4,
+                roleA ? (stat_ok && (!SPARSE || stat > -INFINITY) ? stat * kLog2e : INFINITY) : (stat_ok ? stat : 0.f));
   };
   auto stats_at = [&](auto kc) -> const char* { return lds + stat_off + decltype(kc)::value * (kStepQ * 4); };
   char* const px = lds + S::OFF_PX + slice * 4096 + lane * 16;  // this lane's P slots
@@ -648,11 +673,14 @@ __device__ __forceinline__ void kv16_role(const BwdArgs& a, char* lds) {
   auto probabilities = [&](int j, auto kc) {
     const char* lse2 = stats_at(kc);
     const int q0 = step_q0(j);
+    const bool keep = kept(j);
     const bool need_mask =
         !block_all_visible(q0, q0 + kStepQ - 1, kw0, kw0 + 31, N, CAUSAL, a.wl, a.wr);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      if (need_mask) {
+      if (SPARSE && !keep) {
+        sc[qb] = f32x16{} - INFINITY;
+      } else if (need_mask) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qrow = q0 + 32 * qb + 8 * (r >> 2) + 4 * half + (r & 3);
@@ -707,6 +735,42 @@ __device__ __forceinline__ void kv16_role(const BwdArgs& a, char* lds) {
 #pragma unroll
     for (int p = 0; p < S::NP; ++p) settle(pf[p]);
   };
+
+  auto epilogue = [&]() {
+    // Epilogue: lane = key, registers = head-dim rows of dV^T (A) / dK^T (B).
+    // With several parts per key tile, float32 partials go to the scratch
+    // ([part][B*Hkv][N][d], dK then dV) for bwd_kvsum to add up.
+    if (key >= N) return;
+    const float sc_out = roleA ? 1.f : a.scale;
+    if (parts > 1) {
+      const size_t plane = (size_t)a.B * a.Hkv * N * D;
+      float* prow = a.dkv_part + (roleA ? (size_t)parts * plane : 0) + part * plane + kvhead + (size_t)key * D;
+#pragma unroll
+      for (int dt = 0; dt < S::NDT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x16& v = acc[dt];
+          st<f32x4>(prow + dt * 32 + 8 * g + 4 * half,
+                    f32x4{v[4 * g] * sc_out, v[4 * g + 1] * sc_out, v[4 * g + 2] * sc_out, v[4 * g + 3] * sc_out});
+        }
+      return;
+    }
+    T* row_p = reinterpret_cast<T*>(roleA ? a.dv : a.dk) + kvhead + (size_t)key * D;
+#pragma unroll
+    for (int dt = 0; dt < S::NDT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = dt * 32 + 8 * g + 4 * half;
+        const f32x16& v = acc[dt];
+        st<u32x2>(row_p + d0, u32x2{E::bits(v[4 * g] * sc_out) | ((uint32_t)E::bits(v[4 * g + 1] * sc_out) << 16),
+                                    E::bits(v[4 * g + 2] * sc_out) | ((uint32_t)E::bits(v[4 * g + 3] * sc_out) << 16)});
+      }
+
+  };
+  if (SPARSE && nsteps == 0) {  // no query block keeps these keys: dK = dV = 0
+    epilogue();
+    return;
+  }
 
   // Prologue: stages 0 and 1 in LDS.
   load(0);
@@ -779,43 +843,16 @@ __device__ __forceinline__ void kv16_role(const BwdArgs& a, char* lds) {
   __syncthreads();
   if (roleA) __syncthreads();
 
-  // Epilogue: lane = key, registers = head-dim rows of dV^T (A) / dK^T (B).
-  // With several parts per key tile, float32 partials go to the scratch
-  // ([part][B*Hkv][N][d], dK then dV) for bwd_kvsum to add up.
-  if (key >= N) return;
-  const float sc_out = roleA ? 1.f : a.scale;
-  if (parts > 1) {
-    const size_t plane = (size_t)a.B * a.Hkv * N * D;
-    float* prow = a.dkv_part + (roleA ? (size_t)parts * plane : 0) + part * plane + kvhead + (size_t)key * D;
-#pragma unroll
-    for (int dt = 0; dt < S::NDT; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x16& v = acc[dt];
-        st<f32x4>(prow + dt * 32 + 8 * g + 4 * half,
-                  f32x4{v[4 * g] * sc_out, v[4 * g + 1] * sc_out, v[4 * g + 2] * sc_out, v[4 * g + 3] * sc_out});
-      }
-    return;
-  }
-  T* row_p = reinterpret_cast<T*>(roleA ? a.dv : a.dk) + kvhead + (size_t)key * D;
-#pragma unroll
-  for (int dt = 0; dt < S::NDT; ++dt)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d0 = dt * 32 + 8 * g + 4 * half;
-      const f32x16& v = acc[dt];
-      st<u32x2>(row_p + d0, u32x2{E::bits(v[4 * g] * sc_out) | ((uint32_t)E::bits(v[4 * g + 1] * sc_out) << 16),
-                                  E::bits(v[4 * g + 2] * sc_out) | ((uint32_t)E::bits(v[4 * g + 3] * sc_out) << 16)});
-    }
+  epilogue();
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(kKVThreads, 1) void bwd_kv16_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[KVShape<D>::LDS];
+  __shared__ __attribute__((aligned(16))) char lds[SPARSE ? KVShape<D>::LDS_SPARSE : KVShape<D>::LDS];
   if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 4)
-    kv16_role<T, D, CAUSAL, true>(a, lds);
+    kv16_role<T, D, CAUSAL, SPARSE, true>(a, lds);
   else
-    kv16_role<T, D, CAUSAL, false>(a, lds);
+    kv16_role<T, D, CAUSAL, SPARSE, false>(a, lds);
 }
 
 // dK, dV = the sum of the parts' float32 partials (in part order, so the
@@ -878,16 +915,20 @@ struct DQShape {
   static constexpr int NLD = kDQBN * UNITS / kDQGroup;   // loads per thread per tile
   static_assert(NLD * kDQGroup == kDQBN * UNITS, "even split");
   static_assert(LDS <= 160 * 1024, "LDS budget");
+  // Block-sparse: the list of key blocks and the compaction scratch.
+  static constexpr int OFF_TL = LDS;
+  static constexpr int LDS_SPARSE = OFF_TL + 2 * kMaxMaskBlocks + 4 * 8;
 };
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(kDQThreads, 1) void bwd_dq16_kernel(BwdArgs a) {
   using S = DQShape<D>;
   using E = Elem<T>;
   using Raw = u32x4;
   constexpr int ROWB = S::ROWB;
+  static_assert(kMaskBlock == 2 * kDQBN && kDQBM == 4 * kMaskBlock, "mask blocks of two key tiles");
 
-  __shared__ __attribute__((aligned(16))) char lds[S::LDS];
+  __shared__ __attribute__((aligned(16))) char lds[SPARSE ? S::LDS_SPARSE : S::LDS];
   char* const kbuf = lds;
   char* const vbuf = lds + S::NKBUF * S::TILE;
 
@@ -921,16 +962,46 @@ __global__ __launch_bounds__(kDQThreads, 1) void bwd_dq16_kernel(BwdArgs a) {
   // this wave's rows see tiles [w_lo, w_end) of them (none if past N).
   const int qlast = min(q0 + kDQBM, N) - 1;
   const int t0 = first_visible_key(q0, a.wl) / kDQBN;
-  const int nkv = last_visible_key(qlast, N, CAUSAL, a.wr) / kDQBN - t0 + 1;
+  int nkv = last_visible_key(qlast, N, CAUSAL, a.wr) / kDQBN - t0 + 1;
+  // Block-sparse: the tiles are those of the key blocks in that range that
+  // one of the workgroup's four 64-row query blocks keeps (an LDS list,
+  // entries flagging which); every wave takes all of them, and a wave whose
+  // block drops a tile's block hides all its scores there.
+  const uint16_t* klist = nullptr;
+  const int b0 = t0 / 2;
+  if constexpr (SPARSE) {
+    uint16_t* sl = reinterpret_cast<uint16_t*>(lds + S::OFF_TL);
+    int* sw = reinterpret_cast<int*>(lds + S::OFF_TL + 2 * kMaxMaskBlocks);
+    const int qb0 = q0 / kMaskBlock;
+    const int nb = (t0 + nkv - 1) / 2 - b0 + 1;
+    nkv = 2 * compact_blocks<kDQThreads, 4>(a.block_mask, (long long)qb0 * a.nmb + b0, 1, a.nmb,
+                                            min(kDQBM / kMaskBlock, a.nmb - qb0), nb, sl, sw);
+    klist = sl;
+  }
+  // Key tile of step i, and whether this wave's query block keeps it.
+  auto ktile = [&](int i) -> int {
+    if constexpr (SPARSE) return 2 * (b0 + (__builtin_amdgcn_readfirstlane(klist[i >> 1]) >> 4)) + (i & 1);
+    return t0 + i;
+  };
+  auto kept = [&](int i) -> bool {
+    if constexpr (SPARSE) return (__builtin_amdgcn_readfirstlane(klist[i >> 1]) >> (wave >> 1)) & 1;
+    return true;
+  };
   int w_lo = nkv + 1, w_end = -1;
   if (qw0 < N) {
-    w_lo = first_visible_key(qw0, a.wl) / kDQBN - t0;
-    w_end = last_visible_key(min(qw0 + 31, N - 1), N, CAUSAL, a.wr) / kDQBN - t0 + 1;
+    if (SPARSE) {
+      w_lo = 0;
+      w_end = nkv;
+    } else {
+      w_lo = first_visible_key(qw0, a.wl) / kDQBN - t0;
+      w_end = last_visible_key(min(qw0 + 31, N - 1), N, CAUSAL, a.wr) / kDQBN - t0 + 1;
+    }
   }
 
   // This row's LSE (log2 units) and D; rows past N get LSE = +inf, so their
-  // probabilities (and dS) are exactly 0.
-  const float lr = qrow < N ? a.lse[qhead + qrow] * kLog2e : INFINITY;
+  // probabilities (and dS) are exactly 0 (as do rows that see no key, whose
+  // LSE is -inf).
+  const float lr = qrow < N && (!SPARSE || a.lse[qhead + qrow] > -INFINITY) ? a.lse[qhead + qrow] * kLog2e : INFINITY;
   const float dr = qrow < N ? a.dsum[qhead + qrow] : 0.f;
 
   // Q^T and dO^T as MFMA B operands: lane half h holds head-dim elements
@@ -1014,8 +1085,10 @@ __global__ __launch_bounds__(kDQThreads, 1) void bwd_dq16_kernel(BwdArgs a) {
   // (word w of operand u pairs registers 8u + 2w, 8u + 2w + 1; every word is
   // written after the scores it overwrites were read). Hidden keys get
   // S = -inf, so P = 0 and dS = 0.
-  auto vphase = [&](int k0) {
-    if (!block_all_visible(qw0, qw0 + 31, k0, k0 + kDQBN - 1, N, CAUSAL, a.wl, a.wr)) {
+  auto vphase = [&](int k0, bool keep) {
+    if (SPARSE && !keep) {
+      s = f32x16{} - INFINITY;
+    } else if (!block_all_visible(qw0, qw0 + 31, k0, k0 + kDQBN - 1, N, CAUSAL, a.wl, a.wr)) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = k0 + 8 * (r >> 2) + 4 * half + (r & 3);
@@ -1041,7 +1114,7 @@ __global__ __launch_bounds__(kDQThreads, 1) void bwd_dq16_kernel(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < S::NLD; ++j) {
       const int idx = gtid + kDQGroup * j, row = idx / S::UNITS, u = idx % S::UNITS;
-      stg[j] = X.ld16(((t0 + tile) * kDQBN * D + row * D + u * 8) * 2);
+      stg[j] = X.ld16((ktile(tile) * kDQBN * D + row * D + u * 8) * 2);
     }
   };
   auto lstore = [&](char* tile) {
@@ -1056,6 +1129,28 @@ __global__ __launch_bounds__(kDQThreads, 1) void bwd_dq16_kernel(BwdArgs a) {
   // The same with the buffer a compile-time constant.
   auto kts = [&](auto bc) -> char* { return kbuf + decltype(bc)::value * S::TILE; };
   auto vts = [&](auto bc) -> char* { return vbuf + decltype(bc)::value * S::TILE; };
+
+  // Epilogue: dQ = scale * accumulator; lane = query row, registers =
+  // head-dim rows of dQ^T.
+  auto epilogue = [&]() {
+    if (w_end <= 0 && !SPARSE) return;
+    if (qrow >= N) return;
+    T* qrow_p = dQ + (size_t)qrow * D;
+    const float sc = a.scale;
+#pragma unroll
+    for (int dt = 0; dt < S::NDT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = dt * 32 + 8 * g + 4 * half;
+        const f32x16& v = dq[dt];
+        st<u32x2>(qrow_p + d0, u32x2{E::bits(v[4 * g] * sc) | ((uint32_t)E::bits(v[4 * g + 1] * sc) << 16),
+                                     E::bits(v[4 * g + 2] * sc) | ((uint32_t)E::bits(v[4 * g + 3] * sc) << 16)});
+      }
+  };
+  if (SPARSE && nkv == 0) {  // no key block is kept: dQ = 0
+    epilogue();
+    return;
+  }
 
   // Prologue: K tile 0 (group A), V tiles 0 and 1 (group B).
   const bool kgrp = group == 0;  // group A streams K, group B V
@@ -1087,7 +1182,7 @@ __global__ __launch_bounds__(kDQThreads, 1) void bwd_dq16_kernel(BwdArgs a) {
     if (lt < nkv) gload(X, lt);
     if (w_lo == 0 && w_end > 0) mphase(kt(0), kt(0), vt(0), BoolC<false>{}, BoolC<true>{});
     __syncthreads();
-    if (w_lo == 0 && w_end > 0) vphase(t0 * kDQBN);
+    if (w_lo == 0 && w_end > 0) vphase(ktile(0) * kDQBN, kept(0));
     if (lt < nkv) lstore(kgrp ? kt(lt) : vt(lt));
     __syncthreads();
   }
@@ -1102,7 +1197,7 @@ __global__ __launch_bounds__(kDQThreads, 1) void bwd_dq16_kernel(BwdArgs a) {
     if (w_lo <= i && i <= w_end)
       mphase(kts(IntC<(b + 2) % 3>{}), kts(bc), vts(bc), BoolC<true>{}, BoolC<true>{});
     __syncthreads();
-    if (w_lo <= i && i < w_end) vphase((t0 + i) * kDQBN);
+    if (w_lo <= i && i < w_end) vphase(ktile(i) * kDQBN, kept(i));
     if (lt < nkv) lstore(kgrp ? kts(IntC<(b + 1) % 3>{}) : vts(IntC<(b + 2) % 3>{}));
     __syncthreads();
   };
@@ -1128,21 +1223,7 @@ __global__ __launch_bounds__(kDQThreads, 1) void bwd_dq16_kernel(BwdArgs a) {
   }
   __syncthreads();
   if (kgrp) __syncthreads();
-
-  // Epilogue: dQ = scale * accumulator; lane = query row, registers =
-  // head-dim rows of dQ^T.
-  if (w_end <= 0 || qrow >= N) return;
-  T* qrow_p = dQ + (size_t)qrow * D;
-  const float sc = a.scale;
-#pragma unroll
-  for (int dt = 0; dt < S::NDT; ++dt)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d0 = dt * 32 + 8 * g + 4 * half;
-      const f32x16& v = dq[dt];
-      st<u32x2>(qrow_p + d0, u32x2{E::bits(v[4 * g] * sc) | ((uint32_t)E::bits(v[4 * g + 1] * sc) << 16),
-                                   E::bits(v[4 * g + 2] * sc) | ((uint32_t)E::bits(v[4 * g + 3] * sc) << 16)});
-    }
+  epilogue();
 }
 
 // D_i = sum_k dO_ik O_ik (float32) and dQ accumulator rows cleared.
@@ -1220,8 +1301,10 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)((long long)a.B * a.Hkv * nkt * args.kv_parts));
     const void* fn;
     if constexpr (sizeof(T) == 2)
-      fn = a.causal ? reinterpret_cast<const void*>(&bwd_kv16_kernel<T, D, true>)
-                    : reinterpret_cast<const void*>(&bwd_kv16_kernel<T, D, false>);
+      fn = a.block_mask ? (a.causal ? reinterpret_cast<const void*>(&bwd_kv16_kernel<T, D, true, true>)
+                                    : reinterpret_cast<const void*>(&bwd_kv16_kernel<T, D, false, true>))
+                        : (a.causal ? reinterpret_cast<const void*>(&bwd_kv16_kernel<T, D, true, false>)
+                                    : reinterpret_cast<const void*>(&bwd_kv16_kernel<T, D, false, false>));
     else
       fn = a.causal ? reinterpret_cast<const void*>(&bwd_main_kernel<T, D, true>)
                     : reinterpret_cast<const void*>(&bwd_main_kernel<T, D, false>);
@@ -1241,8 +1324,11 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
     void* kargs[] = {&args};
     const int nqt = (a.N + kDQBM - 1) / kDQBM;
     const dim3 grid((unsigned)((long long)a.B * a.H * nqt));
-    const void* fn = a.causal ? reinterpret_cast<const void*>(&bwd_dq16_kernel<T, D, true>)
-                              : reinterpret_cast<const void*>(&bwd_dq16_kernel<T, D, false>);
+    const void* fn =
+        a.block_mask ? (a.causal ? reinterpret_cast<const void*>(&bwd_dq16_kernel<T, D, true, true>)
+                                 : reinterpret_cast<const void*>(&bwd_dq16_kernel<T, D, false, true>))
+                     : (a.causal ? reinterpret_cast<const void*>(&bwd_dq16_kernel<T, D, true, false>)
+                                 : reinterpret_cast<const void*>(&bwd_dq16_kernel<T, D, false, false>));
     return hipLaunchKernel(fn, grid, dim3(kDQThreads), kargs, 0, stream);
   } else {
     long long n4 = rows * D / 4;

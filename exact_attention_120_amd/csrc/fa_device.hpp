@@ -264,4 +264,37 @@ __device__ inline int xcd_remap(int bid, int total) {
   return x * per + (x < rem ? x : rem) + idx;
 }
 
+// Block-sparse tile lists. All threads of the workgroup (NT of them) call
+// this together. For x = 0 .. n-1 it ORs the ny mask bytes
+// mask[base + x*sx + y*sy] (y = 0 .. ny-1) into a bit field and, for every x
+// with a nonzero field, appends (x << SHIFT) | field to list in increasing x.
+// Returns the count (the same in every thread). wsum is LDS scratch of NT/64
+// ints; list is LDS with room for n entries.
+template <int NT, int SHIFT>
+__device__ inline int compact_blocks(const uint8_t* mask, long long base, int sx, int sy, int ny,
+                                     int n, uint16_t* list, int* wsum) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int total = 0;
+  for (int c0 = 0; c0 < n; c0 += NT) {
+    const int x = c0 + tid;
+    int bits = 0;
+    if (x < n)
+      for (int y = 0; y < ny; ++y) bits |= (mask[base + (long long)x * sx + (long long)y * sy] != 0) << y;
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(bits != 0);
+    const int pre = __builtin_popcountll(bal & ((1ull << lane) - 1));
+    if (lane == 0) wsum[wave] = __builtin_popcountll(bal);
+    __syncthreads();
+    int off = total, chunk = 0;
+    for (int w = 0; w < NW; ++w) {
+      if (w < wave) off += wsum[w];
+      chunk += wsum[w];
+    }
+    if (bits != 0) list[off + pre] = (uint16_t)((x << SHIFT) | bits);
+    total += chunk;
+    __syncthreads();
+  }
+  return total;
+}
+
 }  // namespace fa

@@ -416,7 +416,7 @@ struct GroupStage {
   }
 };
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a) {
   using S = PPShape<T, D>;
   using E = Elem<T>;
@@ -470,6 +470,31 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a) {
     const int hi = min(last_visible_key(min(qw0 + 31, N - 1), N, CAUSAL, a.wr) / kBN - t0 + 1, nkv);
     if (lo < hi) w_lo = lo, w_end = hi;
   }
+  // Block-sparse: the streamed tiles are those of [t0, t0 + nkv) that some
+  // 64-row query block of the workgroup keeps, in order (an LDS list whose
+  // entries also flag which of the four blocks keep the tile); every wave
+  // runs every listed tile and hides all scores of a tile its block drops.
+  const uint16_t* tlist = nullptr;
+  if constexpr (SPARSE) {
+    static_assert(kBN == kMaskBlock && kPPBM == 4 * kMaskBlock, "tiles of one mask block, four per workgroup");
+    __shared__ uint16_t sl[kMaxMaskBlocks];
+    __shared__ int sw[kPPWaves];
+    const int qb0 = q0 / kMaskBlock;
+    const int nyb = min(kPPBM / kMaskBlock, a.nmb - qb0);
+    nkv = compact_blocks<kPPThreads, 4>(a.block_mask, (long long)qb0 * a.nmb + t0, 1, a.nmb, nyb,
+                                        nkv, sl, sw);
+    tlist = sl;
+    if (qw0 < N) w_lo = 0, w_end = nkv;
+  }
+  // Stream position x -> key tile, and whether this wave's block keeps it.
+  auto ktile = [&](int x) -> int {
+    if constexpr (SPARSE) return t0 + (__builtin_amdgcn_readfirstlane(tlist[x]) >> 4);
+    return t0 + x;
+  };
+  auto kept = [&](int x) -> bool {
+    if constexpr (SPARSE) return (__builtin_amdgcn_readfirstlane(tlist[x]) >> ((qw0 - q0) / kMaskBlock)) & 1;
+    return true;
+  };
 
   // Q^T as MFMA B operands: lane half h holds head-dim elements
   // [h*D/2, h*D/2 + D/2) of its row, KH per MFMA.
@@ -570,8 +595,11 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a) {
   };
 
   // Online softmax of one tile: scores s -> probabilities pf.
-  auto softmax = [&](int k0) {
-    if (!block_all_visible(qw0, qw0 + 31, k0, k0 + kBN - 1, N, CAUSAL, a.wl, a.wr)) {
+  auto softmax = [&](int k0, bool keep) {
+    if (SPARSE && !keep) {  // a block this wave's rows do not see
+#pragma unroll
+      for (int mt = 0; mt < S::NMT; ++mt) s[mt] = f32x16{} - INFINITY;
+    } else if (!block_all_visible(qw0, qw0 + 31, k0, k0 + kBN - 1, N, CAUSAL, a.wl, a.wr)) {
       // Diagonal, window edge or tail tile: hidden scores -> -inf (probability 0).
 #pragma unroll
       for (int mt = 0; mt < S::NMT; ++mt)
@@ -642,6 +670,16 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a) {
   };
 
   if (nkv == 0) {  // an empty slice: nothing to visit, an empty partial
+    if constexpr (SPARSE) {  // no kept block: O = 0, LSE = -inf
+      if (qrow < N) {
+#pragma unroll
+        for (int dt = 0; dt < S::NDT; ++dt)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) st<u32x2>(O + (size_t)qrow * D + dt * 32 + 8 * g + 4 * half, u32x2{0u, 0u});
+        if (half == 0) L[qrow] = -INFINITY;
+      }
+      return;
+    }
     if (qrow < N) write_partial(a, split, bh, qrow, half, o, -FLT_MAX, 0.f);
     return;
   }
@@ -650,7 +688,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a) {
   using GS = GroupStage<D>;
   GS stg;
   if (group == 0 || nkv > 1) {
-    stg.load(K, (t0 + group) * kBN, gtid);
+    stg.load(K, ktile(group) * kBN, gtid);
     stg.store(kbuf + group * S::K_BYTES, GS::k_off(gtid), GS::K_STRIDE);
   }
 #pragma unroll
@@ -674,17 +712,17 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a) {
   // d = 64 at the start of the matrix phase that precedes the store
   // (measured 4% faster there).
   constexpr bool kEarlyLoad = D == 128;
-  if (kEarlyLoad && (kgrp ? 2 < nkv : true)) stg.load(X, (t0 + (kgrp ? 2 : 0)) * kBN, gtid);
+  if (kEarlyLoad && (kgrp ? 2 < nkv : true)) stg.load(X, ktile(kgrp ? 2 : 0) * kBN, gtid);
   if (kgrp) __syncthreads();
   // Step 0 (no PV yet).
   {
     const int lt = kgrp ? 2 : 0;
-    if (!kEarlyLoad && lt < nkv) stg.load(X, (t0 + lt) * kBN, gtid);
+    if (!kEarlyLoad && lt < nkv) stg.load(X, ktile(lt) * kBN, gtid);
     if (w_lo == 0 && w_end > 0) mphase(vbuf, kbuf, BoolC<false>{}, BoolC<true>{});
     __syncthreads();
-    if (w_lo == 0 && w_end > 0) softmax(t0 * kBN);
+    if (w_lo == 0 && w_end > 0) softmax(ktile(0) * kBN, kept(0));
     if (lt < nkv) stg.store(kgrp ? kbuf : vbuf, soff, sstride);
-    if (kEarlyLoad && lt + 1 < nkv) stg.load(X, (t0 + lt + 1) * kBN, gtid);
+    if (kEarlyLoad && lt + 1 < nkv) stg.load(X, ktile(lt + 1) * kBN, gtid);
     __syncthreads();
   }
   // Steps 1 .. nkv-1, one code path. At step w_lo (a wave whose first
@@ -693,14 +731,14 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a) {
   // w_end (a wave past its last visible tile) the QK half is unused.
   for (int i = 1; i < nkv; ++i) {
     const int lt = kgrp ? i + 2 : i;  // the tile this group streams
-    if (!kEarlyLoad && lt < nkv) stg.load(X, (t0 + lt) * kBN, gtid);
+    if (!kEarlyLoad && lt < nkv) stg.load(X, ktile(lt) * kBN, gtid);
     if (w_lo <= i && i <= w_end)
       mphase(vbuf + ((i - 1) & 1) * S::V_BYTES, kbuf + (i & 1) * S::K_BYTES, BoolC<true>{},
              BoolC<true>{});
     __syncthreads();
-    if (w_lo <= i && i < w_end) softmax((t0 + i) * kBN);
+    if (w_lo <= i && i < w_end) softmax(ktile(i) * kBN, kept(i));
     if (lt < nkv) stg.store(kgrp ? kbuf + (i & 1) * S::K_BYTES : vbuf + (i & 1) * S::V_BYTES, soff, sstride);
-    if (kEarlyLoad && lt + 1 < nkv) stg.load(X, (t0 + lt + 1) * kBN, gtid);
+    if (kEarlyLoad && lt + 1 < nkv) stg.load(X, ktile(lt + 1) * kBN, gtid);
     __syncthreads();
   }
   // Final matrix phase: PV of the last tile.
@@ -714,7 +752,8 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a) {
     write_partial(a, split, bh, qrow, half, o, m, lt);
     return;
   }
-  const float inv = 1.0f / lt;
+  // (Block-sparse: a row that kept no key has l = 0: O = 0, LSE = -inf.)
+  const float inv = SPARSE && !(lt > 0.f) ? 0.f : 1.0f / lt;
   T* orow = O + (size_t)qrow * D;
 #pragma unroll
   for (int dt = 0; dt < S::NDT; ++dt)
@@ -725,7 +764,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a) {
       const uint32_t w1 = E::bits(o[dt][4 * g + 2] * inv) | ((uint32_t)E::bits(o[dt][4 * g + 3] * inv) << 16);
       st<u32x2>(orow + d0, u32x2{w0, w1});
     }
-  if (half == 0) L[qrow] = m * a.scale + logf(lt);
+  if (half == 0) L[qrow] = SPARSE && !(lt > 0.f) ? -INFINITY : m * a.scale + logf(lt);
 }
 
 // Split-KV merge of the partials of every row: with M = max_s LSE_s and
@@ -776,7 +815,8 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   void* kargs[] = {&args};
   const void* fn;
   if constexpr (kPP)
-    fn = reinterpret_cast<const void*>(&fwd_pp_kernel<T, D, CAUSAL>);
+    fn = a.block_mask ? reinterpret_cast<const void*>(&fwd_pp_kernel<T, D, CAUSAL, true>)
+                      : reinterpret_cast<const void*>(&fwd_pp_kernel<T, D, CAUSAL, false>);
   else
     fn = reinterpret_cast<const void*>(&fwd_kernel<T, D, CAUSAL>);
   hipError_t e = hipLaunchKernel(fn, grid, dim3(kPP ? kPPThreads : kThreads), kargs, 0, stream);

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime_api.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace fa {
 
@@ -34,6 +35,11 @@ struct FwdArgs {
   // factor of V; scale / scale_log2 then already hold the product of the
   // softmax scale and the factors of Q and K.
   float v_descale = 1.f;
+  // Block-sparse attention: nonzero bytes of block_mask [nmb][nmb] (64-row
+  // query block x 64-key block, shared by all batches and heads) mark the
+  // blocks whose scores are kept; nullptr = dense.
+  const uint8_t* block_mask = nullptr;
+  int nmb = 0;
 };
 
 // Backward: forward tensors plus dO and the gradient outputs. `dsum` is the
@@ -62,6 +68,8 @@ struct BwdArgs {
   // workgroups, each part's dK and dV land here before being summed.
   float* dkv_part = nullptr;
   int kv_parts = 1;  // workgroups per key tile (set by the launcher)
+  const uint8_t* block_mask = nullptr;  // as in FwdArgs
+  int nmb = 0;
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
@@ -70,6 +78,9 @@ hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 
 long long fwd_grid_size(int B, int H, int N);
+
+constexpr int kMaskBlock = 64;        // block-sparse mask granularity (rows and keys)
+constexpr int kMaxMaskBlocks = 1024;  // block-sparse calls: N <= 65536
 
 // Rows per forward workgroup and the split count the library picks for a
 // shape: enough workgroups to occupy every compute unit once, with at least

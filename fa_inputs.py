@@ -18,6 +18,10 @@ Recipe (the same for every workload):
 8-bit float inputs (``make_fp8_inputs``) start from the same float32 draws
 and store each tensor as OCP E4M3 codes with one per-tensor factor.
 
+Block masks (``make_block_mask``) are byte maps over 64-row x 64-key blocks
+in a few structured families (random, banded, banded plus global blocks,
+striped, with empty block rows), drawn with a numpy generator of their own.
+
 The named workloads are the five shapes the scope names: a tiny fp32 head, a
 causal bf16 head batch at N=1024, a non-causal bf16 batch at N=4096 with
 inputs scaled by 0.5, a long-sequence bf16 batch at N=16384 (non-causal and
@@ -127,6 +131,47 @@ def make_fp8_inputs(B: int, H: int, N: int, d: int, *, seed: int = 0,
         descale.append(float(s))
     out["descale"] = tuple(descale)
     return out
+
+
+MASK_KINDS = ("random", "band", "band_global", "stripes", "empty_rows", "dense", "diagonal")
+
+
+def make_block_mask(N: int, kind: str, *, seed: int = 0, density: float = 0.5,
+                    block: int = 64) -> torch.Tensor:
+    """A [ceil(N/block)]^2 uint8 CPU tensor; nonzero = the (query block, key
+    block) pair is kept.
+
+    ``random``: each pair kept with probability ``density``, block (0, 0)
+    always. ``band``: |i - j| <= 2 blocks. ``band_global``: the band plus
+    block row and column 0 plus random pairs at density / 4. ``stripes``:
+    key blocks j with j % 3 == i % 3. ``empty_rows``: ``random`` with every
+    third block row dropped entirely (those query rows see no key).
+    ``dense``: all ones. ``diagonal``: i == j only.
+    """
+    import numpy as np
+
+    nb = -(-N // block)
+    rng = np.random.default_rng(seed)
+    i, j = np.meshgrid(np.arange(nb), np.arange(nb), indexing="ij")
+    if kind == "random":
+        m = rng.random((nb, nb)) < density
+        m[0, 0] = True
+    elif kind == "band":
+        m = np.abs(i - j) <= 2
+    elif kind == "band_global":
+        m = (np.abs(i - j) <= 2) | (i == 0) | (j == 0) | (rng.random((nb, nb)) < density / 4)
+    elif kind == "stripes":
+        m = (j % 3) == (i % 3)
+    elif kind == "empty_rows":
+        m = rng.random((nb, nb)) < density
+        m[1::3, :] = False
+    elif kind == "dense":
+        m = np.ones((nb, nb), dtype=bool)
+    elif kind == "diagonal":
+        m = i == j
+    else:
+        raise ValueError(f"unknown mask kind {kind!r}")
+    return torch.from_numpy(m.astype(np.uint8)).contiguous()
 
 
 def workload_inputs(w: Workload) -> dict:

@@ -264,6 +264,46 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                float q_descale, float k_descale, float v_descale, int out_dtype,
                const fa_options* opts, void* stream);
 
+/*
+ * Block-sparse attention.
+ *
+ * The pages name block-sparse attention among the method's extensions
+ * (section 6.1 "稀疏注意力变体" of "FlashAttention：优化大模型训练的内存与计算
+ * 效率") without fixing a format. Here the pattern is a map over blocks of
+ * FA_MASK_BLOCK query rows by FA_MASK_BLOCK keys: with nmb = ceil(N / 64),
+ * block_mask is a row-major [nmb, nmb] array of bytes in device memory, the
+ * same for every batch and head, and
+ *   key j is hidden from query i  if  block_mask[i / 64][j / 64] == 0,
+ * on top of the causal rule, the window and grouped heads of fa_options. The
+ * kernels never visit a key tile that every query row of a workgroup has
+ * dropped, as the pages' section 二.7 skips the tiles above the causal
+ * diagonal. A query row that sees no key at all gets O = 0 and LSE = -inf,
+ * and its gradient terms are 0 (dQ = 0; it adds nothing to dK or dV).
+ *
+ * fa_fwd_sparse -- fa_fwd_ex under a block mask.
+ * fa_bwd_sparse -- fa_bwd_ex under the same block mask (scale, causal, opts
+ *                  and block_mask must match the forward call that produced
+ *                  o and lse).
+ *   block_mask : [nmb, nmb] bytes, device memory, read-only, owned by the
+ *                caller; no alignment needed; it must not overlap any output
+ *                or the workspace.
+ *   other arguments as for fa_fwd_ex / fa_bwd_ex.
+ * Status: as fa_fwd_ex / fa_bwd_ex, plus block_mask NULL or overlapping an
+ * output -> FA_ERR_INVALID_ARG; dtype FA_F32 or N > 65536 (nmb > 1024)
+ * -> FA_ERR_UNSUPPORTED.
+ */
+#define FA_MASK_BLOCK 64
+
+int fa_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int N, int d, float scale, int causal, int dtype,
+                  const fa_options* opts, const void* block_mask, void* stream);
+
+int fa_bwd_sparse(const void* q, const void* k, const void* v, const void* o,
+                  const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                  int B, int H, int N, int d, float scale, int causal, int dtype,
+                  const fa_options* opts, const void* block_mask, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
 /* fa_strerror -- static, NUL-terminated description of a status code. */
 const char* fa_strerror(int status);
 

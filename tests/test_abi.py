@@ -28,7 +28,7 @@ def test_header_functions_are_exported(lib):
     names = _lib.header_functions()
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_fwd_ex", "fa_bwd_ex", "fa_bwd_workspace_size",
                           "fa_fwd_num_splits", "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv",
-                          "fa_fwd_fp8", "fa_strerror"}
+                          "fa_fwd_fp8", "fa_fwd_sparse", "fa_bwd_sparse", "fa_strerror"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -289,3 +289,65 @@ FWD_FP8_CASES = [
 def test_fwd_fp8_rejects(lib, kw, status):
     assert fwd_fp8(lib, **kw) == status
 
+
+
+MASK = 0x10_0000_0000 + 10 * 0x1_0000_0000  # fake block-mask address (never dereferenced)
+
+
+def fwd_sparse(lib, mask=MASK, q=Q, o=O, lse=LSE, B=1, H=4, N=16, d=64, causal=0, dtype=2,
+               kv_heads=0, opts=True):
+    op = ctypes.byref(_lib.FaOptions(kv_heads, -1, -1)) if opts else None
+    return lib.fa_fwd_sparse(q, K, V, o, lse, B, H, N, d, 0.125, causal, dtype, op, mask, None)
+
+
+def bwd_sparse(lib, mask=MASK, dq=DQ, dk=DK, ws=WS, B=1, H=4, N=16, d=64, causal=0, dtype=1,
+               kv_heads=0):
+    op = ctypes.byref(_lib.FaOptions(kv_heads, -1, -1))
+    wsb = lib.fa_bwd_workspace_size(B, H, N, d)
+    return lib.fa_bwd_sparse(Q, K, V, O, DO, LSE, dq, dk, DV, B, H, N, d, 0.125, causal, dtype,
+                             op, mask, ws, wsb, None)
+
+
+FWD_SPARSE_CASES = [
+    (dict(mask=None), FA_ERR_INVALID_ARG),
+    (dict(q=None), FA_ERR_INVALID_ARG),
+    (dict(dtype=0), FA_ERR_UNSUPPORTED),          # float32 is not offered
+    (dict(dtype=7), FA_ERR_INVALID_ARG),
+    (dict(N=65537), FA_ERR_UNSUPPORTED),          # 1025 mask blocks
+    (dict(d=96), FA_ERR_UNSUPPORTED),
+    (dict(kv_heads=3), FA_ERR_INVALID_ARG),
+    (dict(o=O + 8), FA_ERR_ALIGN),
+    (dict(mask=O + 4096), FA_ERR_INVALID_ARG),    # the mask inside o
+    (dict(mask=LSE + 16), FA_ERR_INVALID_ARG),    # the mask inside lse
+    (dict(mask=O - 1, N=100), FA_ERR_INVALID_ARG),  # 2x2 blocks: its last 3 bytes are in o
+]
+
+
+@pytest.mark.parametrize("kw,status", FWD_SPARSE_CASES)
+def test_fwd_sparse_rejects(lib, kw, status):
+    assert fwd_sparse(lib, **kw) == status
+
+
+def test_fwd_sparse_mask_extent_is_nmb_squared_bytes(lib):
+    # N = 16384: 256 x 256 blocks, 65536 bytes. A mask starting 65535 bytes
+    # before lse reaches into it; one 2^16 bytes before would not (not called:
+    # that would launch).
+    assert fwd_sparse(lib, mask=LSE - 65535, N=16384) == FA_ERR_INVALID_ARG
+
+
+BWD_SPARSE_CASES = [
+    (dict(mask=None), FA_ERR_INVALID_ARG),
+    (dict(dtype=0), FA_ERR_UNSUPPORTED),
+    (dict(N=70000), FA_ERR_UNSUPPORTED),
+    (dict(kv_heads=3), FA_ERR_INVALID_ARG),
+    (dict(dk=DK + 4), FA_ERR_ALIGN),
+    (dict(mask=DQ + 256), FA_ERR_INVALID_ARG),    # inside dq
+    (dict(mask=DK), FA_ERR_INVALID_ARG),          # at dk
+    (dict(mask=WS + 100), FA_ERR_INVALID_ARG),    # inside the workspace
+    (dict(ws=WS + 1), FA_ERR_ALIGN),
+]
+
+
+@pytest.mark.parametrize("kw,status", BWD_SPARSE_CASES)
+def test_bwd_sparse_rejects(lib, kw, status):
+    assert bwd_sparse(lib, **kw) == status
