@@ -396,17 +396,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
 constexpr int kStepQ = 64;  // query rows per inner step of the dK/dV kernel
 
 // XOR swizzle of the 16-byte units of a tile row (ROWB bytes per row, 256 or
-// 128). Conflict-free for 16 lanes reading 16 bytes from 16 consecutive rows
-// (a bijection on row mod 16 over the units of a 256-byte bank line), and
-// for 16 lanes reading 4 consecutive 4-aligned rows x 32 bytes (the four
-// rows' unit pairs land on disjoint banks).
+// 128), for LDS's 64 four-byte banks (one 256-byte bank line per cycle).
+// Conflict-free for 16 lanes reading 16 bytes from 16 consecutive rows (a
+// bijection on row mod 16, or on row pair mod 8, over the units of a bank
+// line), and for the transposing 8-byte reads, which the LDS serves 32 lanes
+// at a time: those lanes read 4 consecutive 4-aligned rows x 64 bytes, and
+// the swizzle puts the four rows' 4-unit groups on disjoint banks. (A swizzle
+// that separated only 16-lane groups left 2-way conflicts there, measured as
+// about a fifth of the backward kernels' LDS-busy cycles.)
 template <int ROWB>
 __device__ constexpr int row_swz(int row) {
   if constexpr (ROWB == 256) {
-    return ((row & 3) << 1) | ((row >> 2) & 1) | (((row >> 3) & 1) << 3);
+    return ((row & 3) << 2) | ((row >> 2) & 3);
   } else {
     const int m = row >> 1;  // two 128-byte rows share a bank line
-    return ((m & 1) << 1) | ((m >> 1) & 1) | (m & 4);
+    return ((m & 1) << 2) | ((m >> 1) & 3);
   }
 }
 
