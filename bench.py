@@ -29,6 +29,7 @@ reported in the same unit.
 Other modes (used to collect the rocprofv3 summaries under profiles/):
   --only fwd|bwd        time only that direction (no CPU baseline)
   --sweep               forward over N in {1k,2k,4k,8k,16k}, B=1 H=16 d=128
+  --sweep-bwd           the same for the backward (after one forward per N)
   --variants            split-KV, grouped K/V heads, a local window and the
                         8-bit float forward against the plain calls (one JSON
                         line per case)
@@ -233,6 +234,29 @@ def run_sweep(args):
                 fa.fa_fwd(q, k, v, o, lse, 128 ** -0.5, causal)
             torch.cuda.synchronize()
             print(json.dumps({"sweep_N": n, "causal": causal}), flush=True)
+
+
+def run_sweep_bwd(args):
+    """Backward over N in {1k, 2k, 4k, 8k, 16k}, B=1 H=16 d=128, both causal
+    settings: one forward for O and LSE, then three fa_bwd calls (for the
+    HBM-bytes-versus-N counters)."""
+    import torch
+
+    import exact_attention_120_amd as fa
+    from fa_inputs import make_inputs
+
+    for n in (1024, 2048, 4096, 8192, 16384):
+        for causal in (False, True):
+            inp = make_inputs(1, 16, n, 128, "bf16", seed=0, backward=True)
+            q, k, v, do = (inp[x].to("cuda:0") for x in ("q", "k", "v", "do"))
+            o, lse = torch.empty_like(q), torch.empty((1, 16, n), device="cuda:0")
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            ws = torch.empty(fa.fa_bwd_workspace_size(1, 16, n, 128), dtype=torch.uint8, device="cuda:0")
+            fa.fa_fwd(q, k, v, o, lse, 128 ** -0.5, causal)
+            for _ in range(3):
+                fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, 128 ** -0.5, causal, ws)
+            torch.cuda.synchronize()
+            print(json.dumps({"sweep_bwd_N": n, "causal": causal}), flush=True)
 
 
 def run_variants(args):
@@ -476,6 +500,7 @@ def main():
     p.add_argument("--only", choices=["fwd", "bwd"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--sweep", action="store_true")
+    p.add_argument("--sweep-bwd", action="store_true")
     p.add_argument("--variants", action="store_true")
     p.add_argument("--fp8", action="store_true")
     p.add_argument("--copy-bytes", type=int)
@@ -492,6 +517,8 @@ def main():
         return run_copy(args)
     if args.sweep:
         return run_sweep(args)
+    if args.sweep_bwd:
+        return run_sweep_bwd(args)
     if args.variants:
         return run_variants(args)
     if args.fp8:
