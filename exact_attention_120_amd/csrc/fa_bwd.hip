@@ -1007,6 +1007,10 @@ __global__ __launch_bounds__(kDQThreads, 1) void bwd_dq16_kernel(BwdArgs a) {
   // LSE is -inf).
   const float lr = qrow < N && (!SPARSE || a.lse[qhead + qrow] > -INFINITY) ? a.lse[qhead + qrow] * kLog2e : INFINITY;
   const float dr = qrow < N ? a.dsum[qhead + qrow] : 0.f;
+  // -D in every register of this lane's column: the dP^T products start
+  // from it, so the accumulator holds dP - D and dS = P * (dP - D) takes
+  // one multiply per score.
+  const f32x16 negd = f32x16{} - dr;
 
   // Q^T and dO^T as MFMA B operands: lane half h holds head-dim elements
   // [h*D/2, h*D/2 + D/2) of its row, 8 per MFMA.
@@ -1068,7 +1072,7 @@ __global__ __launch_bounds__(kDQThreads, 1) void bwd_dq16_kernel(BwdArgs a) {
       } else {
         const int j = cc - NDQC, pr = j / QKH, h = j % QKH;
         f32x16& acc = pr == 0 ? s : dp;
-        if (h == 0) acc = f32x16{};
+        if (h == 0) acc = pr == 0 ? f32x16{} : negd;
 #pragma unroll
         for (int u = 0; u < 4; ++u) acc = E::mma(src[u], pr == 0 ? qf[4 * h + u] : gf[4 * h + u], acc);
       }
@@ -1085,7 +1089,8 @@ __global__ __launch_bounds__(kDQThreads, 1) void bwd_dq16_kernel(BwdArgs a) {
     __builtin_amdgcn_s_setprio(0);
   };
 
-  // Vector phase: dS = P * (dP - D) for the current tile, packed into s
+  // Vector phase: dS = P * (dP - D) for the current tile (dp already holds
+  // dP - D), packed into s
   // (word w of operand u pairs registers 8u + 2w, 8u + 2w + 1; every word is
   // written after the scores it overwrites were read). Hidden keys get
   // S = -inf, so P = 0 and dS = 0.
@@ -1105,7 +1110,7 @@ __global__ __launch_bounds__(kDQThreads, 1) void bwd_dq16_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float p = __builtin_amdgcn_exp2f(fmaf(s[8 * u + e], c, -lr));
-        d[e] = p * (dp[8 * u + e] - dr);
+        d[e] = p * dp[8 * u + e];
       }
 #pragma unroll
       for (int w = 0; w < 4; ++w) s[4 * u + w] = __builtin_bit_cast(float, E::pack_pair(d[2 * w], d[2 * w + 1]));
