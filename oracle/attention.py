@@ -282,49 +282,54 @@ def attention_backward(q, k, v, do, scale: float, causal: bool, window=None, blo
 
 
 def _head_blockwise(q, k, v, scale, causal, block_q, block_k):
-    """One-pass blockwise attention with the online-softmax recurrence.
+    """Tiled one-pass attention for one head: each query tile's result is
+    built up one key tile at a time, never holding more than one tile of
+    scores.
 
-    Loop order: query blocks outer, key/value blocks inner ([FA-principle §二.7],
-    the second FA2 change). Blocks lying entirely in the hidden upper triangle
-    are skipped ([FA-principle §二.7], third change). Per block, following the
-    answer "写一个flashattention算子" step 4 (online softmax) and step 5
-    (incremental output update), in its notation:
-      m_ij = rowmax(S_ij); p_ij = exp(S_ij - m_ij); l_ij = rowsum(p_ij)
-      m_new = max(m_prev, m_ij)
-      l_new = exp(m_prev - m_new) l_prev + exp(m_ij - m_new) l_ij
-      O_i   = (exp(m_prev - m_new) l_prev O_prev + exp(m_ij - m_new) p_ij V_j) / l_new
+    Loop order: query tiles outer, key tiles inner, and tiles that lie wholly
+    above the causal diagonal are never visited ([FA-principle] §二.7, the
+    FA2 changes). How a key tile is folded in ([FA-principle] §二.5-§二.6,
+    tiling with a blockwise softmax; the answer "写一个flashattention算子",
+    steps 4-5): the state of a query tile is a pair (acc_o, acc_lse), the
+    attention output normalized over the keys folded in so far and the
+    log-normalizer of those keys. A key tile yields its own pair
+    (tile_o, tile_lse), the softmax restricted to its keys. Two pairs over
+    disjoint key sets combine into the pair over their union: the new
+    log-normalizer is the log-sum-exp of the two, and each output is weighted
+    by exp(own log-normalizer - new one) -- the rescaling by the change of
+    the running maximum and sum, carried as logarithms. A row that sees no
+    key of a tile has tile_lse = -inf and weight 0 there.
     """
-    n, nk = q.shape[0], k.shape[0]
-    o = np.zeros((n, v.shape[1]))
+    n, nk, dv = q.shape[0], k.shape[0], v.shape[1]
+    o = np.zeros((n, dv))
     lse = np.empty(n)
     for i0 in range(0, n, block_q):
-        i1 = min(i0 + block_q, n)
-        qi = q[i0:i1]
-        m_prev = np.full((i1 - i0, 1), -np.inf)
-        l_prev = np.zeros((i1 - i0, 1))
-        o_prev = np.zeros((i1 - i0, v.shape[1]))
+        rows = np.arange(i0, min(i0 + block_q, n))
+        acc_o = np.zeros((rows.size, dv))
+        acc_lse = np.full(rows.size, -np.inf)
         for j0 in range(0, nk, block_k):
-            j1 = min(j0 + block_k, nk)
-            if causal and j0 > i1 - 1:
-                continue                       # block fully above the diagonal
-            vis = None
+            keys = np.arange(j0, min(j0 + block_k, nk))
+            if causal and keys[0] > rows[-1]:
+                continue                      # tile wholly above the diagonal
+            s = scale * (q[rows] @ k[keys].T)
             if causal:
-                vis = np.arange(j0, j1)[None, :] <= np.arange(i0, i1)[:, None]
-            s_ij = scale * (qi @ k[j0:j1].T)
-            if vis is not None:
-                s_ij = np.where(vis, s_ij, -np.inf)
-            m_ij = s_ij.max(axis=1, keepdims=True)
-            seen = np.isfinite(m_ij)           # rows with >= 1 visible key here
-            p_ij = np.where(seen, np.exp(s_ij - np.where(seen, m_ij, 0.0)), 0.0)
-            l_ij = p_ij.sum(axis=1, keepdims=True)
-            m_new = np.maximum(m_prev, m_ij)
-            a_prev = np.where(np.isfinite(m_prev), np.exp(m_prev - m_new), 0.0)
-            a_ij = np.where(seen, np.exp(m_ij - m_new), 0.0)
-            l_new = a_prev * l_prev + a_ij * l_ij
-            o_prev = (a_prev * l_prev * o_prev + a_ij * (p_ij @ v[j0:j1])) / l_new
-            m_prev, l_prev = m_new, l_new
-        o[i0:i1] = o_prev
-        lse[i0:i1] = (m_prev + np.log(l_prev))[:, 0]
+                s = np.where(keys[None, :] <= rows[:, None], s, -np.inf)
+            top = s.max(axis=1)
+            sees = np.isfinite(top)           # rows with a visible key in this tile
+            shift = np.where(sees, top, 0.0)
+            w = np.exp(s - shift[:, None])    # hidden keys: exp(-inf) = 0
+            tot = np.where(sees, w.sum(axis=1), 1.0)
+            tile_o = (w @ v[keys]) / tot[:, None]
+            tile_lse = np.where(sees, shift + np.log(tot), -np.inf)
+            new_lse = np.logaddexp(acc_lse, tile_lse)
+            live = np.isfinite(new_lse)
+            ref = np.where(live, new_lse, 0.0)
+            keep_acc = np.where(np.isfinite(acc_lse), np.exp(acc_lse - ref), 0.0)
+            keep_tile = np.where(sees, np.exp(tile_lse - ref), 0.0)
+            acc_o = keep_acc[:, None] * acc_o + keep_tile[:, None] * tile_o
+            acc_lse = new_lse
+        o[rows] = acc_o
+        lse[rows] = acc_lse
     return o, lse
 
 
@@ -342,8 +347,8 @@ def merge_partials(o_a, lse_a, o_b, lse_b):
 
     Each part is normalized over its own keys and carries its LSE; the total
     normalizer is the log-sum of both, and each part is reweighted by
-    exp(LSE_part - LSE_total). This is the step-5 correction of the answer
-    "写一个flashattention算子" applied to two finished partial results.
+    exp(LSE_part - LSE_total): the same fold of two disjoint key sets that
+    _head_blockwise applies tile by tile, here to two finished results.
     """
     o_a, lse_a, o_b, lse_b = _f64(o_a), _f64(lse_a), _f64(o_b), _f64(lse_b)
     lse = np.logaddexp(lse_a, lse_b)

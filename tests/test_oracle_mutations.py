@@ -56,12 +56,18 @@ MUTATIONS = [
     ("dQ without scale", "dq[r0:r1] = scale * (ds @ k)", "dq[r0:r1] = (ds @ k)"),
     ("dV with P not transposed", "dv += p.T @ do[r0:r1]", "dv += p @ do[r0:r1]"),
     ("dP uses K in place of V", "dp = do[r0:r1] @ v.T", "dp = do[r0:r1] @ k.T"),
-    ("recurrence drops the old sum", "l_new = a_prev * l_prev + a_ij * l_ij",
-     "l_new = l_prev + a_ij * l_ij"),
-    ("recurrence skips needed blocks", "if causal and j0 > i1 - 1:",
-     "if causal and j0 > i0:"),
-    ("recurrence forgets old output", "o_prev = (a_prev * l_prev * o_prev + a_ij",
-     "o_prev = (a_prev * o_prev + a_ij"),
+    ("recurrence keeps the larger normalizer instead of their sum",
+     "new_lse = np.logaddexp(acc_lse, tile_lse)", "new_lse = np.maximum(acc_lse, tile_lse)"),
+    ("recurrence skips needed tiles", "if causal and keys[0] > rows[-1]:",
+     "if causal and keys[0] > rows[0]:"),
+    ("recurrence forgets the old output",
+     "acc_o = keep_acc[:, None] * acc_o + keep_tile[:, None] * tile_o",
+     "acc_o = keep_tile[:, None] * tile_o"),
+    ("recurrence does not reweight the tile",
+     "acc_o = keep_acc[:, None] * acc_o + keep_tile[:, None] * tile_o",
+     "acc_o = keep_acc[:, None] * acc_o + tile_o"),
+    ("tile output left unnormalized", "tile_o = (w @ v[keys]) / tot[:, None]",
+     "tile_o = (w @ v[keys])"),
     ("merge weight inverted", "w_a = np.exp(lse_a - lse)[..., None]",
      "w_a = np.exp(lse - lse_a)[..., None]"),
 ]
