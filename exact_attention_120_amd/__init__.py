@@ -117,11 +117,21 @@ def _kv_shape(q, k):
     return B, H, Hkv, N, d
 
 
+_INT32_MAX = 2 ** 31 - 1
+
+
 def _options(Hkv: int, window):
+    """fa_options for Hkv K/V heads and window (left, right); None or a
+    negative bound is unbounded. Bounds must fit the C int: a larger one
+    would wrap in ctypes, so it is rejected here."""
     wl, wr = (None, None) if window is None else window
-    wl = -1 if wl is None or wl < 0 else int(wl)
-    wr = -1 if wr is None or wr < 0 else int(wr)
-    return _lib.FaOptions(Hkv, wl, wr)
+    bounds = []
+    for name, b in (("left", wl), ("right", wr)):
+        if b is not None and int(b) > _INT32_MAX:
+            raise ValueError(f"window {name} bound {b} does not fit a 32-bit int "
+                             "(any bound >= N - 1 is unbounded; pass None or -1)")
+        bounds.append(-1 if b is None or b < 0 else int(b))
+    return _lib.FaOptions(Hkv, bounds[0], bounds[1])
 
 
 def fa_fwd_ex(q, k, v, o, lse, scale: float, causal: bool, window=None, stream=None) -> None:

@@ -57,14 +57,19 @@ int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 struct Opts {
   int Hkv, wl, wr;
 };
-int read_opts(const fa_options* o, int H, Opts* out) {
+// A window bound of N - 1 or more hides nothing on its side, so it is the
+// same as no bound; mapping it to -1 keeps the kernels' index sums (query
+// +/- bound) within int for every accepted bound up to INT_MAX.
+int window_bound(int b, int N) { return b < 0 || b >= N - 1 ? -1 : b; }
+
+int read_opts(const fa_options* o, int H, int N, Opts* out) {
   out->Hkv = H;
   out->wl = out->wr = -1;
   if (!o) return FA_OK;
   if (o->kv_heads < 0 || (o->kv_heads > 0 && H % o->kv_heads != 0)) return FA_ERR_INVALID_ARG;
   out->Hkv = o->kv_heads == 0 ? H : o->kv_heads;
-  out->wl = o->window_left < 0 ? -1 : o->window_left;
-  out->wr = o->window_right < 0 ? -1 : o->window_right;
+  out->wl = window_bound(o->window_left, N);
+  out->wr = window_bound(o->window_right, N);
   return FA_OK;
 }
 
@@ -85,7 +90,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   int st = check_shape(B, H, N, d, scale, causal, dtype);
   if (st != FA_OK) return st;
   Opts op;
-  if ((st = read_opts(opts, H, &op)) != FA_OK) return st;
+  if ((st = read_opts(opts, H, N, &op)) != FA_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_ALIGN;
   const size_t tb = (size_t)B * H * N * d * elem_size(dtype);
@@ -119,7 +124,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
   int st = check_shape(B, H, N, d, scale, causal, dtype);
   if (st != FA_OK) return st;
   Opts op;
-  if ((st = read_opts(opts, H, &op)) != FA_OK) return st;
+  if ((st = read_opts(opts, H, N, &op)) != FA_OK) return st;
   const void* ptrs[] = {q, k, v, o, dO, lse, dq, dk, dv};
   for (const void* p : ptrs)
     if (!aligned16(p)) return FA_ERR_ALIGN;
@@ -194,7 +199,7 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   const float score_scale = scale * q_descale * k_descale;
   if (!isfinite(score_scale)) return FA_ERR_INVALID_ARG;
   Opts op;
-  if ((st = read_opts(opts, H, &op)) != FA_OK) return st;
+  if ((st = read_opts(opts, H, N, &op)) != FA_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_ALIGN;
   const size_t qb = (size_t)B * H * N * d;
@@ -235,7 +240,7 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
   int st = check_shape(B, H, N, d, scale, causal, dtype);
   if (st != FA_OK) return st;
   Opts op;
-  if ((st = read_opts(opts, H, &op)) != FA_OK) return st;
+  if ((st = read_opts(opts, H, N, &op)) != FA_OK) return st;
   if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_INVALID_ARG;
   const int ns = num_splits == 0 ? fa::fwd_auto_splits(B, H, N, dtype) : num_splits;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))

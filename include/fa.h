@@ -141,6 +141,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
  *   window_right : >= 0: key j is hidden from query i if j > i + window_right.
  *                  Negative: no bound on that side. The window combines with
  *                  ``causal`` (causal alone is the window (unbounded, 0)).
+ * A bound of N - 1 or more hides no key on its side and is treated as
+ * unbounded, so every int value is accepted for either bound.
  * Every query row sees at least its own key (a non-negative bound never
  * excludes j = i). Key tiles that lie entirely outside every query's window
  * are never visited: they generalize the causal tile skipping of the pages'

@@ -181,6 +181,30 @@ def test_bwd_ex_rejects(lib, kw, status):
     assert bwd_ex(lib, **kw) == status
 
 
+INT_MAX = 2 ** 31 - 1
+
+
+@pytest.mark.parametrize("wl,wr", [(INT_MAX, 0), (0, INT_MAX), (INT_MAX, INT_MAX),
+                                   (15, 15), (1 << 30, -5)])
+def test_any_int_window_bound_is_accepted(lib, wl, wr):
+    # A bound of N - 1 or more is the unbounded side; every int is valid, so
+    # the single defect (a misaligned q) is still the one reported.
+    assert fwd_ex(lib, wl=wl, wr=wr, q=Q + 8) == FA_ERR_ALIGN
+    assert bwd_ex(lib, wl=wl, wr=wr, dq=DQ + 2) == FA_ERR_ALIGN
+    assert bwd_ex(lib, wl=wl, wr=wr, kv_heads=3) == FA_ERR_INVALID_ARG
+
+
+def test_binding_window_bounds_must_fit_int32():
+    import exact_attention_120_amd as fa
+    op = fa._options(4, (INT_MAX, None))
+    assert (op.kv_heads, op.window_left, op.window_right) == (4, INT_MAX, -1)
+    op = fa._options(4, (-7, 3))
+    assert (op.window_left, op.window_right) == (-1, 3)
+    for window in ((INT_MAX + 1, 0), (0, 2 ** 32 + 5), (2 ** 40, 2 ** 40)):
+        with pytest.raises(ValueError):
+            fa._options(4, window)
+
+
 def test_ex_with_null_options_validates_like_plain(lib):
     # NULL options = plain attention; the same single defects are rejected.
     assert fwd_ex(lib, opts=False, q=None) == FA_ERR_INVALID_ARG
