@@ -1,10 +1,9 @@
 """GPU parity of fa_bwd against the CPU oracle's analytic gradients (float64
 on the same rounded inputs), called through the C ABI via the binding.
 
-Tolerances (max abs error): bf16/fp16 dQ, dK, dV <= 5e-2 (the scope's bound);
-fp32 <= 1e-4 (fp32 MFMA products and float32 accumulation of O(1) terms over
-up to a few thousand keys: a few 1e-6 relative; 1e-4 leaves margin for the
-atomic summation order of dQ).
+Tolerances (max abs error, the scope's bounds): bf16/fp16 dQ, dK, dV <= 5e-2;
+fp32 dQ, dK, dV <= 1e-5 (the scope's fp32 bound holds for every fp32 result).
+Every check prints its measured maxima.
 """
 
 import numpy as np
@@ -17,7 +16,7 @@ from oracle import attention_backward
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-4, "f16": 5e-2, "bf16": 5e-2}
+TOL = {"f32": 1e-5, "f16": 5e-2, "bf16": 5e-2}
 DEV = "cuda"
 
 
@@ -44,6 +43,8 @@ def check(got, ref, dtype, what=""):
         g64 = to_f64(g) if isinstance(g, torch.Tensor) else g
         assert np.isfinite(g64).all(), f"{what} {name} has non-finite values"
         errs[name] = float(np.abs(g64 - r).max())
+    print(f"  {what} {dtype} gradient max errors: "
+          + ", ".join(f"{k} {e:.3e}" for k, e in errs.items()), flush=True)
     bad = {k: e for k, e in errs.items() if not e <= TOL[dtype]}
     assert not bad, f"{what} max errors {errs}"
     return errs
@@ -72,19 +73,39 @@ def test_fp16_causal_workload_full():
     print(f"[bwd workload] {w.name}: {errs}", flush=True)
 
 
+_FULL = {}
+
+
+def _full_size(name):
+    """Inputs and GPU gradients of a full-size workload, computed once per
+    module (the launch covers every head; the head groups below each check
+    part of it)."""
+    if name not in _FULL:
+        _FULL.clear()
+        w = WORKLOADS[name]
+        inp = make_inputs(w.B, w.H, w.N, w.d, w.dtype, seed=w.seed, input_scale=w.input_scale,
+                          backward=True)
+        got = [g.cpu() for g in run(inp, w.causal, w.scale)]
+        _FULL[name] = (w, inp, got)
+    return _FULL[name]
+
+
 @pytest.mark.parametrize("name", ["bf16_n4k_d128", "bf16_n16k_d128", "bf16_n16k_d128_causal"])
-def test_full_size_bf16_one_head(name):
-    """Full-size launch (every head); the oracle checks the last head whole."""
-    w = WORKLOADS[name]
-    print(f"\n[bwd full-size] {w}", flush=True)
-    inp = make_inputs(w.B, w.H, w.N, w.d, w.dtype, seed=w.seed, input_scale=w.input_scale,
-                      backward=True)
-    got = run(inp, w.causal, w.scale)
-    b, h = w.B - 1, w.H - 1
-    ref = attention_backward(*(to_f64(inp[n][b, h]) for n in ("q", "k", "v", "do")),
-                             w.scale, w.causal)
-    errs = check([to_f64(g[b, h]) for g in got], ref[:3], w.dtype, name)
-    print(f"[bwd full-size] {name}: {errs}", flush=True)
+@pytest.mark.parametrize("part", range(4))
+def test_full_size_bf16_every_head(name, part):
+    """Full-size launch; the oracle checks every head whole, a quarter of the
+    (batch, head) pairs per test case."""
+    w, inp, got = _full_size(name)
+    print(f"\n[bwd full-size] {w} heads part {part}/4", flush=True)
+    pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
+    n = len(pairs) // 4
+    worst = {}
+    for b, h in pairs[part * n:(part + 1) * n]:
+        ref = attention_backward(*(to_f64(inp[x][b, h]) for x in ("q", "k", "v", "do")),
+                                 w.scale, w.causal)
+        errs = check([to_f64(g[b, h]) for g in got], ref[:3], w.dtype, f"{name} b={b} h={h}")
+        worst = {k: max(worst.get(k, 0.0), e) for k, e in errs.items()}
+    print(f"[bwd full-size] {name} part {part}: {worst}", flush=True)
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -106,9 +127,11 @@ def test_scale_zero(dtype):
     check(got, ref[:3], dtype)
 
 
-def test_dk_dv_deterministic_dq_close():
-    inp = make_inputs(2, 2, 700, 128, "bf16", seed=13, backward=True)
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_16bit_backward_is_deterministic(dtype):
+    """The 16-bit backward has no atomics: dQ, dK and dV repeat bit for bit."""
+    inp = make_inputs(2, 2, 700, 128, dtype, seed=13, backward=True)
     a = run(inp, True, scale_of(128))
     b = run(inp, True, scale_of(128), poison_workspace=False)
-    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
-    assert (a[0].float() - b[0].float()).abs().max().item() < 1e-2  # atomic order only
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)

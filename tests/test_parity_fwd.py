@@ -75,16 +75,9 @@ def test_workload_forward(name):
     inp = workload_inputs(w)
     o, lse = run_fwd(inp, w.causal, w.scale)
     q, k, v = (to_f64(inp[n]) for n in ("q", "k", "v"))
-    if w.N <= 2048:
-        ref_o, ref_l = attention_forward(q, k, v, w.scale, w.causal)
-        rows = None
-    else:
-        # Full-size launch, checked on sampled rows the oracle computes
-        # exactly (every head, the same sampled rows incl. tile edges).
-        rows = sampled_rows(w.N, 96, 1)
-        ref_o, ref_l = attention_forward(q[..., rows, :], k, v, w.scale, w.causal,
-                                         q_positions=rows)
-    err = check(o, lse, ref_o, ref_l, w.dtype, rows)
+    # Every row of every head against the oracle (row-chunked on the host).
+    ref_o, ref_l = attention_forward(q, k, v, w.scale, w.causal)
+    err = check(o, lse, ref_o, ref_l, w.dtype)
     print(f"[fwd workload] {name}: max|dO|={err[0]:.3e} max|dLSE|={err[1]:.3e}", flush=True)
 
 
