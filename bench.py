@@ -106,10 +106,93 @@ def cpu_baseline(w, inputs, budget_s=10.0, max_s=30.0):
             break
     el = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
-    return {"value": flop / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    cores = len(os.sched_getaffinity(0))
+    return {"value": flop / el / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "blas_threads": threads,
             "sample": f"float64 numpy oracle, forward + backward of {heads} of {w.B * w.H} "
-                      f"heads (all {w.N} rows each) of this workload, {el:.1f} s; host has "
-                      f"{len(os.sched_getaffinity(0))} cores, BLAS threads {threads}"}
+                      f"heads (all {w.N} rows each) of this workload, {el:.1f} s; "
+                      f"{cores} host cores available, BLAS threads {threads}"}
+
+
+def per_call_ms(fn, min_s=0.25, max_calls=4096):
+    """Mean duration of fn() (one library call on the current stream), from
+    HIP events around back-to-back calls: doubles the call count until the
+    timed batch lasts at least min_s."""
+    import torch
+
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    n = 1
+    while True:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        if ms * 1e-3 >= min_s or n >= max_calls:
+            return ms / n
+        n *= 2
+
+
+def config_rates(peak):
+    """Forward (and where the workload has one, backward) rates of every named
+    workload other than the headline one, and a TFLOP/s-versus-N sweep, each
+    timed with HIP events on the stream the calls run on. Returns a dict for
+    the JSON line."""
+    import torch
+
+    import exact_attention_120_amd as fa
+    from fa_inputs import WORKLOADS, make_inputs, workload_inputs
+
+    dev = torch.device("cuda:0")
+
+    def rates(q, k, v, do, scale, causal, fwd_flop, with_bwd, pk):
+        B, H, N, d = q.shape
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        f_ms = per_call_ms(lambda: fa.fa_fwd(q, k, v, o, lse, scale, causal))
+        r = {"fwd_ms": f_ms, "fwd_tflops": fwd_flop / (f_ms * 1e-3) / 1e12}
+        r["fwd_frac_of_peak"] = r["fwd_tflops"] / pk
+        if with_bwd:
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device=dev)
+            b_ms = per_call_ms(lambda: fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale, causal,
+                                                 ws))
+            r.update(bwd_ms=b_ms, bwd_tflops=2.5 * fwd_flop / (b_ms * 1e-3) / 1e12)
+            r["bwd_frac_of_peak"] = r["bwd_tflops"] / pk
+        return r
+
+    out = {}
+    for name, with_bwd in (("tiny_f32", False), ("causal_bf16_n1k", False),
+                           ("bf16_n4k_d128", True), ("bf16_n16k_d128_causal", True),
+                           ("f16_n2k_fwdbwd_causal", True)):
+        w = WORKLOADS[name]
+        inp = workload_inputs(type(w)(**{**w.__dict__, "backward": True}))
+        q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+        pk = PEAK_TFLOPS[w.dtype]
+        r = rates(q, k, v, do, w.scale, w.causal, w.fwd_flops(), with_bwd, pk)
+        out[name] = dict({"B": w.B, "H": w.H, "N": w.N, "d": w.d, "dtype": w.dtype,
+                          "causal": w.causal}, **r)
+        del q, k, v, do, inp
+    # Sequence-length sweep, bf16 d=128, 16384 tokens per call (B = 16384/N,
+    # H = 16), both causal settings; inputs N(0,1) drawn on the device from a
+    # seeded generator (timing only).
+    sweep = []
+    g = torch.Generator(device=dev)
+    for N in (512, 1024, 2048, 4096, 8192, 16384):
+        B, H, d = 16384 // N, 16, 128
+        g.manual_seed(N)
+        q, k, v, do = (torch.randn((B, H, N, d), generator=g, device=dev).to(torch.bfloat16)
+                       for _ in range(4))
+        for causal in (False, True):
+            fl = 4.0 * B * H * N * N * d / (2 if causal else 1)
+            r = rates(q, k, v, do, 128 ** -0.5, causal, fl, True, PEAK_TFLOPS["bf16"])
+            sweep.append(dict({"B": B, "H": H, "N": N, "d": d, "causal": causal}, **r))
+        del q, k, v, do
+    return out, sweep
 
 
 def time_calls(fn, steps, warmup, events_per_call, warmup_s=0.0):
@@ -214,6 +297,8 @@ def run_main(args):
     out["roofline"] = dict(roofs[dominant], direction=dominant)
     for name, r in roofs.items():
         out["roofline_" + name] = r
+    if args.only is None and not args.no_configs:
+        out["configs"], out["sweep_bf16_d128"] = config_rates(peak)
     if args.only is None and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(out), flush=True)
@@ -272,22 +357,8 @@ def run_variants(args):
 
     dev = torch.device("cuda:0")
 
-    def per_call_ms(fn, min_s=0.4):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        n, t0 = 1, time.time()
-        while True:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(n):
-                fn()
-            e1.record()
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1)
-            if ms * 1e-3 >= min_s or time.time() - t0 > 5 * min_s:
-                return ms / n
-            n *= 2
+    def per_call_ms(fn):
+        return globals()["per_call_ms"](fn, min_s=0.4)
 
     # Split-KV: the library's slice count and fixed counts against fa_fwd.
     for (B, H, N, d, causal) in ((2, 8, 1024, 64, True), (1, 8, 2048, 128, False),
@@ -499,6 +570,8 @@ def main():
     p.add_argument("--workload", default="bf16_n16k_d128")
     p.add_argument("--only", choices=["fwd", "bwd"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the other workloads' rates and the N sweep")
     p.add_argument("--sweep", action="store_true")
     p.add_argument("--sweep-bwd", action="store_true")
     p.add_argument("--variants", action="store_true")
