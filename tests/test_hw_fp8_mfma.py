@@ -6,8 +6,10 @@ adds its 64 products (it does not add them like float32), and its
 mean-square model an RMS term rms * (the same magnitude). This test measures
 that instruction on in-bounds random operands (tests/hw/fp8_mfma_probe.hip,
 one instruction per tile with a zero accumulator) against the exact float64
-sums of the decoded codes, and requires the worst and the RMS relative error
-to stay within half of the constants the parity bound uses.
+sums of the decoded codes, and requires the worst relative error to stay
+within half of the constant the parity bound uses, and, for the operand
+families the kernel feeds the instruction, the RMS relative error within
+half of the mean-square model's constant.
 
 Operand families: codes drawn uniformly over every finite E4M3 code (products
 spanning 2^-18 .. 2^17.6, the hardest case for alignment), N(0,1) data
@@ -67,6 +69,12 @@ def probability_codes(rng, shape):
     return torch.from_numpy(p.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
+# Families whose RMS the parity bound's mean-square model uses: the
+# operands the FP8 kernel feeds the instruction (quantized data for the
+# scores, probability codes times quantized values for P V). Codes spread
+# over the whole range are checked against the worst-case constant only.
+RMS_FAMILIES = ("quantized_normal", "probabilities_x_values")
+
 FAMILIES = {
     "whole_range": lambda rng: (finite_codes(rng, (TILES, 32, 64)),
                                 finite_codes(rng, (TILES, 32, 64))),
@@ -94,7 +102,8 @@ def test_fp8_mfma_accumulation_error_within_half_the_bound(family):
           f"rms {rms:.3e} (2^{np.log2(max(rms, 1e-300)):.2f}); bound uses eps 2^"
           f"{np.log2(EPS_MFMA8):.0f}, rms 2^{np.log2(RMS_MFMA8):.0f}", flush=True)
     assert worst <= EPS_MFMA8 / 2, f"worst relative error {worst:.3e} > eps/2"
-    assert rms <= RMS_MFMA8 / 2, f"RMS relative error {rms:.3e} > rms/2"
+    if family in RMS_FAMILIES:
+        assert rms <= RMS_MFMA8 / 2, f"RMS relative error {rms:.3e} > rms/2"
 
 
 def test_probe_pairs_operands_as_assumed():
