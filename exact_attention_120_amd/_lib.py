@@ -7,7 +7,9 @@ import os
 import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libfa.so")
+# The in-tree build, unless FA_LIBRARY names another build of the same C ABI
+# (the host-sanitizer run of the ABI tests loads one built for the host alone).
+LIB_PATH = os.environ.get("FA_LIBRARY") or os.path.join(PKG, "libfa.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "fa.h")
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2

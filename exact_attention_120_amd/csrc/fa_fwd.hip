@@ -835,21 +835,8 @@ hipError_t dispatch_d(const FwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
-long long fwd_grid_size(int B, int H, int N) {
-  return (long long)B * H * ((N + kBM - 1) / kBM);
-}
-
-int fwd_rows_per_workgroup(int dtype) { return dtype == 0 ? kBM : kPPBM; }
-
-int fwd_auto_splits(int B, int H, int N, int dtype) {
-  constexpr int kCUs = 256;
-  const int bm = fwd_rows_per_workgroup(dtype);
-  const long long wgs = (long long)B * H * ((N + bm - 1) / bm);
-  const int nkt = (N + kBN - 1) / kBN;
-  int s = 1;
-  while (s < 16 && wgs * s < kCUs && nkt / (2 * s) >= 4) s *= 2;
-  return s;
-}
+static_assert(kBM == kFwdRowsF32 && kPPBM == kFwdRows16 && kBN == kFwdKeyTile,
+              "host-side grid arithmetic (fa_host.cpp) uses these tile sizes");
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   switch (a.dtype) {

@@ -77,6 +77,13 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 
+// Forward tile sizes, shared with the host-side grid arithmetic
+// (fa_host.cpp): query rows per workgroup (float32 kernel, 16-bit kernel)
+// and keys per tile.
+constexpr int kFwdRowsF32 = 128;
+constexpr int kFwdRows16 = 256;
+constexpr int kFwdKeyTile = 64;
+
 long long fwd_grid_size(int B, int H, int N);
 
 constexpr int kMaskBlock = 64;        // block-sparse mask granularity (rows and keys)
