@@ -28,7 +28,8 @@ from . import _lib
 
 __all__ = ["FaError", "fa_fwd", "fa_bwd", "fa_fwd_ex", "fa_bwd_ex", "fa_bwd_workspace_size",
            "fa_fwd_num_splits", "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv",
-           "fa_fwd_fp8", "fa_fwd_sparse", "fa_bwd_sparse", "fa_strerror", "forward",
+           "fa_fwd_fp8", "fa_fwd_sparse", "fa_bwd_sparse", "fa_bwd_noalloc", "fa_strerror",
+           "forward",
            "forward_fp8", "backward", "DTYPES", "FP8_DTYPES", "MASK_BLOCK"]
 
 DTYPES = {torch.float32: _lib.FA_F32, torch.float16: _lib.FA_F16,
@@ -104,6 +105,24 @@ def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool, workspac
                                 workspace.numel() * workspace.element_size(), _stream(q, stream))
     if st != _lib.FA_OK:
         raise FaError(st, "fa_bwd")
+
+
+def fa_bwd_noalloc(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool,
+                   stream=None) -> None:
+    """fa_bwd without a workspace: the library's static per-GPU scratch is
+    used instead (no allocation at all; calls overlapping in time on one GPU
+    race). Raises FaError (FA_ERR_SCRATCH) for problems too large for it."""
+    B, H, N, d = _shape(q)
+    _check({"q": q, "k": k, "v": v, "o": o, "do": do, "dq": dq, "dk": dk, "dv": dv},
+           (B, H, N, d), q.dtype)
+    _check({"lse": lse}, (B, H, N), torch.float32)
+    with torch.cuda.device(q.device):
+        st = _lib.load().fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                        do.data_ptr(), lse.data_ptr(), dq.data_ptr(),
+                                        dk.data_ptr(), dv.data_ptr(), B, H, N, d, float(scale),
+                                        int(bool(causal)), DTYPES[q.dtype], _stream(q, stream))
+    if st != _lib.FA_OK:
+        raise FaError(st, "fa_bwd_noalloc")
 
 
 def _kv_shape(q, k):

@@ -47,6 +47,8 @@ SIGNATURES = {
                              _opt, _vp, _vp]),
     "fa_bwd_sparse": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int,
                              _flt, _int, _int, _opt, _vp, _vp, _sz, _vp]),
+    "fa_bwd_noalloc": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int,
+                              _flt, _int, _int, _vp]),
     "fa_strerror": (_c.c_char_p, [_int]),
 }
 

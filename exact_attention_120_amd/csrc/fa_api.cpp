@@ -115,11 +115,21 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   return hip_status(fa::launch_fwd(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
+// Scratch bytes of the plain backward (no grouped K/V heads) when the
+// library supplies them: D, plus the float32 dQ accumulator for FA_F32 (the
+// 16-bit kernels write dQ directly; without grouped heads nothing is split).
+size_t plain_scratch_bytes(int B, int H, int N, int d, int dtype) {
+  const size_t rows = (size_t)B * H * N;
+  return round_up(rows * sizeof(float)) + (dtype == FA_F32 ? round_up(rows * d * sizeof(float)) : 0);
+}
+
+// workspace == nullptr with static_ws: the library's static scratch
+// (fa_bwd_noalloc; opts and mask are then NULL).
 int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dO,
              const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
              float scale, int causal, int dtype, const fa_options* opts, const void* mask,
-             void* workspace, size_t workspace_bytes, void* stream) {
-  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv || !workspace)
+             void* workspace, size_t workspace_bytes, void* stream, bool static_ws = false) {
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv || (!workspace && !static_ws))
     return FA_ERR_INVALID_ARG;
   int st = check_shape(B, H, N, d, scale, causal, dtype);
   if (st != FA_OK) return st;
@@ -128,9 +138,14 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
   const void* ptrs[] = {q, k, v, o, dO, lse, dq, dk, dv};
   for (const void* p : ptrs)
     if (!aligned16(p)) return FA_ERR_ALIGN;
-  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return FA_ERR_ALIGN;
-  const size_t need = fa_bwd_workspace_size(B, H, N, d);
-  if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+  size_t need = 0;
+  if (static_ws) {
+    if (plain_scratch_bytes(B, H, N, d, dtype) > fa::kStaticScratchBytes) return FA_ERR_SCRATCH;
+  } else {
+    if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return FA_ERR_ALIGN;
+    need = fa_bwd_workspace_size(B, H, N, d);
+    if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+  }
 
   const size_t tb = (size_t)B * H * N * d * elem_size(dtype);
   const size_t kb = (size_t)B * op.Hkv * N * d * elem_size(dtype);
@@ -143,6 +158,10 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
       if (overlap(w.p, w.n, r.p, r.n)) return FA_ERR_INVALID_ARG;
     for (const Range& x : outs)
       if (&x != &w && overlap(w.p, w.n, x.p, x.n)) return FA_ERR_INVALID_ARG;
+  }
+  if (static_ws) {  // validated: now look up this GPU's scratch (no allocation)
+    const hipError_t e = fa::static_scratch(&workspace);
+    if (e != hipSuccess) return FA_ERR_HIP;
   }
 
   char* ws = static_cast<char*>(workspace);
@@ -308,6 +327,13 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
                    workspace, workspace_bytes, stream);
 }
 
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                   const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                   float scale, int causal, int dtype, void* stream) {
+  return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, nullptr,
+                  nullptr, nullptr, 0, stream, true);
+}
+
 const char* fa_strerror(int status) {
   switch (status) {
     case FA_OK: return "success";
@@ -316,6 +342,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_ALIGN: return "pointer not sufficiently aligned";
     case FA_ERR_WORKSPACE: return "workspace too small";
     case FA_ERR_HIP: return "HIP runtime error at launch";
+    case FA_ERR_SCRATCH: return "problem too large for the library's static scratch";
     default: return "unknown status";
   }
 }

@@ -24,6 +24,8 @@
 // per key tile), bwd_dq (accumulator * scale -> dQ).
 #include <float.h>
 
+#include <mutex>
+
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
@@ -1353,7 +1355,35 @@ hipError_t dispatch_d(const BwdArgs& a, hipStream_t s) {
   return a.d == 64 ? launch_all<T, 64>(a, s) : launch_all<T, 128>(a, s);
 }
 
+// The library's own scratch for fa_bwd_noalloc (callers that cannot
+// allocate): a file-scope device array, one copy per GPU, held until the
+// process ends. Host code never passes its name to a kernel (in host code
+// the name is a host-side stand-in); it passes the device address that
+// hipGetSymbolAddress returns for the current GPU.
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+
 }  // namespace
+
+hipError_t static_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   switch (a.dtype) {

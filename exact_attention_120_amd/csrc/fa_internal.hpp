@@ -73,6 +73,12 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+
+// fa_bwd_noalloc's scratch: the device address, on the current GPU, of the
+// library's static device array of kStaticScratchBytes bytes (looked up once
+// per GPU, then cached). Allocates nothing.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+hipError_t static_scratch(void** ptr);
 // E4M3 q, k, v (bytes); a.dtype is the output type (fp16 or bf16).
 hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);

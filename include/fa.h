@@ -34,7 +34,8 @@
  *   - Ownership: the caller allocates and owns every buffer (device memory).
  *     The library allocates no device memory, frees nothing and keeps no
  *     pointer after returning. Inputs are read-only; outputs must not overlap
- *     any input or each other.
+ *     any input or each other. (fa_bwd_noalloc alone uses a scratch array
+ *     the library holds statically, one per GPU; see there.)
  *   - Streams: ``stream`` is a hipStream_t (NULL = the null stream). Every
  *     call only enqueues work on it and returns; the results are ready when
  *     the stream is synchronized. The returned status covers argument
@@ -45,14 +46,15 @@
  *     16-bit inputs on bf16/fp16 matrix cores (fp32 matrix cores for FA_F32)
  *     with float32 accumulation; softmax statistics in float32; outputs
  *     rounded to nearest-even into ``dtype``.
- *   - Thread safety: no global mutable state; concurrent calls on different
- *     streams are independent.
+ *   - Thread safety: concurrent calls on different streams are independent,
+ *     except fa_bwd_noalloc calls on one GPU, which share its static scratch.
  *   - Validation (in order; the first failure is returned and nothing is
  *     enqueued): null pointers, B/H/N < 1 or dtype unknown or causal not 0/1
  *     or scale negative/non-finite -> FA_ERR_INVALID_ARG; d not supported or
  *     sizes too large -> FA_ERR_UNSUPPORTED; a pointer not 16-byte aligned
  *     -> FA_ERR_ALIGN; overlapping output/input ranges -> FA_ERR_INVALID_ARG;
- *     workspace too small -> FA_ERR_WORKSPACE.
+ *     workspace too small -> FA_ERR_WORKSPACE (fa_bwd_noalloc: a problem
+ *     too large for its static scratch -> FA_ERR_SCRATCH).
  */
 #ifndef FA_H
 #define FA_H
@@ -73,7 +75,8 @@ enum {
   FA_ERR_UNSUPPORTED = -2,
   FA_ERR_ALIGN = -3,
   FA_ERR_WORKSPACE = -4,
-  FA_ERR_HIP = -5
+  FA_ERR_HIP = -5,
+  FA_ERR_SCRATCH = -6
 };
 
 /*
@@ -118,13 +121,39 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d);
  *                    it needs on ``stream``) and undefined on exit.
  *   other arguments as for fa_fwd (scale and causal must match the forward).
  * The probabilities are recomputed on chip from Q, K and LSE (never read
- * from memory); key/value tiles are the outer (grid) dimension, query tiles
- * the inner loop, and dQ is accumulated in float32 in the workspace.
+ * from memory). bf16/fp16: dK and dV come from a kernel with key tiles as
+ * the outer (grid) dimension and query tiles in the inner loop, dQ from a
+ * kernel with query tiles outer and key tiles inner; no atomics, so the
+ * results repeat bit for bit. float32: one key-outer kernel that adds dQ
+ * into a float32 accumulator in the workspace.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const void* dO, const float* lse, void* dq, void* dk, void* dv,
            int B, int H, int N, int d, float scale, int causal, int dtype,
            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_bwd_noalloc -- fa_bwd without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc). Same arguments, results
+ * and kernels as fa_bwd, except that the scratch (the float32 row term D,
+ * and for FA_F32 the float32 dQ accumulator) lives in the library's own
+ * static device array of 64 MiB, one per GPU, held until the process ends.
+ * Nothing is allocated or freed by the call.
+ *   Limit: 4*B*H*N bytes (bf16, fp16) or 4*B*H*N*(d+1) bytes (FA_F32), each
+ *   part rounded up to 256, must fit in 64 MiB; larger problems return
+ *   FA_ERR_SCRATCH before anything is enqueued (use fa_bwd with a workspace).
+ *   Concurrency: every call on one GPU uses that GPU's one array, so calls
+ *   that overlap in time on one GPU (different streams, or threads) race and
+ *   must be serialized by the caller; calls in one stream are ordered. The
+ *   array keeps the last call's contents; each call writes what it reads
+ *   before reading it (D, and the zeroed accumulator for FA_F32) with
+ *   kernels on ``stream`` (no memset nodes).
+ */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                   const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                   int B, int H, int N, int d, float scale, int causal, int dtype,
+                   void* stream);
 
 /*
  * Variants: grouped K/V heads and local windows.

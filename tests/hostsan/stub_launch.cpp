@@ -1,5 +1,5 @@
-// stub_launch.cpp -- the kernel launchers of fa_internal.hpp replaced by
-// stubs that launch nothing, so that the C-ABI layer (fa_api.cpp) and the
+// stub_launch.cpp -- the kernel launchers of fa_internal.hpp (and the
+// static-scratch lookup) replaced by stubs that touch no device, so that the C-ABI layer (fa_api.cpp) and the
 // host grid arithmetic (fa_host.cpp) can be built for the host alone, with
 // AddressSanitizer and UndefinedBehaviorSanitizer, and driven by the ABI
 // tests on a machine without a GPU. A call that passes validation reaches a
@@ -12,5 +12,6 @@ namespace fa {
 hipError_t launch_fwd(const FwdArgs&, hipStream_t) { return hipErrorInvalidDeviceFunction; }
 hipError_t launch_fwd_fp8(const FwdArgs&, hipStream_t) { return hipErrorInvalidDeviceFunction; }
 hipError_t launch_bwd(const BwdArgs&, hipStream_t) { return hipErrorInvalidDeviceFunction; }
+hipError_t static_scratch(void**) { return hipErrorNoDevice; }
 
 }  // namespace fa

@@ -14,6 +14,7 @@ from exact_attention_120_amd import _lib
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_WORKSPACE, FA_ERR_HIP = (
     0, -1, -2, -3, -4, -5)
+FA_ERR_SCRATCH = -6
 
 # Distinct, 256-byte aligned fake addresses far apart (never dereferenced).
 Q, K, V, O, LSE, DO, DQ, DK, DV, WS = (0x10_0000_0000 + i * 0x1_0000_0000 for i in range(10))
@@ -28,7 +29,8 @@ def test_header_functions_are_exported(lib):
     names = _lib.header_functions()
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_fwd_ex", "fa_bwd_ex", "fa_bwd_workspace_size",
                           "fa_fwd_num_splits", "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv",
-                          "fa_fwd_fp8", "fa_fwd_sparse", "fa_bwd_sparse", "fa_strerror"}
+                          "fa_fwd_fp8", "fa_fwd_sparse", "fa_bwd_sparse", "fa_bwd_noalloc",
+                          "fa_strerror"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -36,7 +38,7 @@ def test_header_functions_are_exported(lib):
 
 def test_strerror(lib):
     for st in (FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_WORKSPACE,
-               FA_ERR_HIP):
+               FA_ERR_HIP, FA_ERR_SCRATCH):
         assert lib.fa_strerror(st) and lib.fa_strerror(st) != b"unknown status"
     assert lib.fa_strerror(12345) == b"unknown status"
 
@@ -111,6 +113,45 @@ BWD_CASES = [
 @pytest.mark.parametrize("kw,status", BWD_CASES)
 def test_bwd_rejects(lib, kw, status):
     assert bwd(lib, **kw) == status
+
+
+def bwd_noalloc(lib, q=Q, k=K, v=V, o=O, do=DO, lse=LSE, dq=DQ, dk=DK, dv=DV, B=1, H=2, N=16,
+                d=64, scale=0.125, causal=1, dtype=1):
+    return lib.fa_bwd_noalloc(q, k, v, o, do, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype,
+                              None)
+
+
+SCRATCH = 64 << 20
+BWD_NOALLOC_CASES = [
+    (dict(do=None), FA_ERR_INVALID_ARG),
+    (dict(dq=None), FA_ERR_INVALID_ARG),
+    (dict(N=0), FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), FA_ERR_INVALID_ARG),
+    (dict(d=96), FA_ERR_UNSUPPORTED),
+    (dict(dk=DK + 4), FA_ERR_ALIGN),
+    (dict(dq=Q), FA_ERR_INVALID_ARG),
+    (dict(dv=DK), FA_ERR_INVALID_ARG),
+    # Too large for the static scratch: D alone (16-bit) or D + the float32
+    # dQ accumulator (FA_F32) exceeds 64 MiB. (Sizes are valid otherwise.)
+    (dict(B=64, H=64, N=4097, d=64), FA_ERR_SCRATCH),                # 4*B*H*N > 64 MiB
+    (dict(B=1, H=2, N=65536, d=128, dtype=0), FA_ERR_SCRATCH),       # fp32: 4*rows*(d+1)
+    # ... and a defect earlier in the validation order still wins.
+    (dict(B=64, H=64, N=4097, d=64, q=Q + 8), FA_ERR_ALIGN),
+]
+
+
+@pytest.mark.parametrize("kw,status", BWD_NOALLOC_CASES)
+def test_bwd_noalloc_rejects(lib, kw, status):
+    assert bwd_noalloc(lib, **kw) == status
+
+
+def test_bwd_noalloc_limit_is_the_scratch_size(lib):
+    # 16-bit: 4*B*H*N bytes may be at most 64 MiB, i.e. 2^24 rows; one row
+    # group past that is rejected before anything is enqueued. (No call
+    # here is valid: a valid one would launch.)
+    rows = SCRATCH // 4
+    assert bwd_noalloc(lib, B=1, H=256, N=rows // 256 + 1, d=64) == FA_ERR_SCRATCH
+    assert bwd_noalloc(lib, B=1, H=256, N=rows // 256, d=64, dk=DK + 2) == FA_ERR_ALIGN
 
 
 def test_signatures_match_header_argument_counts():
