@@ -500,7 +500,8 @@ __device__ __forceinline__ void kv16_role(const BwdArgs& a, char* lds) {
   const int N = a.N;
   const int nkt = (N + kBN - 1) / kBN;
   const int parts = a.kv_parts;  // workgroups sharing one key tile's query heads
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int lin = CAUSAL ? xcd_remap_ranked(blockIdx.x, gridDim.x, nkt * parts, parts)
+                         : xcd_remap(blockIdx.x, gridDim.x);
   const int bkv = lin / (nkt * parts);  // batch * Hkv + K/V head
   const int k0 = lin % (nkt * parts) / parts * kBN;
   const int part = lin % parts;
@@ -940,7 +941,8 @@ __global__ __launch_bounds__(kDQThreads, 1) void bwd_dq16_kernel(BwdArgs a) {
 
   const int N = a.N;
   const int nqt = (N + kDQBM - 1) / kDQBM;
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int lin = CAUSAL ? xcd_remap_ranked(blockIdx.x, gridDim.x, nqt, 1)
+                         : xcd_remap(blockIdx.x, gridDim.x);
   const int bh = lin / nqt;
   const int qtile = CAUSAL ? nqt - 1 - lin % nqt : lin % nqt;
   const int q0 = qtile * kDQBM;

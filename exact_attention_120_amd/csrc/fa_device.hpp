@@ -264,6 +264,24 @@ __device__ inline int xcd_remap(int bid, int total) {
   return x * per + (x < rem ? x : rem) + idx;
 }
 
+// Causal grids: the work of a unit (a query tile in the forward and the dQ
+// kernel, a key tile in the dK/dV kernel) falls with its rank r (r = 0 the
+// longest), and a head has per_head = R * inner units, unit (r, i) at
+// r * inner + i (i: a split slice or a grouped-head part, equal work). Where
+// every XCD holds whole heads (total = 8 * hpx * per_head), each XCD takes
+// its hpx heads rank by rank across the heads (all rank-0 units first), so
+// the longest units start first on every XCD and the short ones fill the
+// end; otherwise the plain remap. A bijection on [0, total) either way.
+__device__ inline int xcd_remap_ranked(int bid, int total, int per_head, int inner) {
+  constexpr int X = 8;
+  if (total % (X * per_head) != 0) return xcd_remap(bid, total);
+  const int hpx = total / (X * per_head);  // heads per XCD
+  const int x = bid % X, idx = bid / X;
+  const int rank = idx / (hpx * inner), rem = idx % (hpx * inner);
+  const int hl = rem / inner, in = rem % inner;
+  return (x * hpx + hl) * per_head + rank * inner + in;
+}
+
 // Block-sparse tile lists. All threads of the workgroup (NT of them) call
 // this together. For x = 0 .. n-1 it ORs the ny mask bytes
 // mask[base + x*sx + y*sy] (y = 0 .. ny-1) into a bit field and, for every x

@@ -429,8 +429,9 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a) {
 
   const int N = a.N;
   const int nqt = (N + kPPBM - 1) / kPPBM;
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int nsplit = a.num_splits;
+  const int lin = CAUSAL ? xcd_remap_ranked(blockIdx.x, gridDim.x, nqt * nsplit, nsplit)
+                         : xcd_remap(blockIdx.x, gridDim.x);
   const int bh = lin / (nqt * nsplit);
   const int qi = lin % (nqt * nsplit) / nsplit, split = lin % nsplit;
   const int qtile = CAUSAL ? nqt - 1 - qi : qi;

@@ -136,7 +136,8 @@ __global__ __launch_bounds__(kF8Threads, 1) void fwd_fp8_kernel(FwdArgs a) {
 
   const int N = a.N;
   const int nqt = (N + kF8BM - 1) / kF8BM;
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int lin = CAUSAL ? xcd_remap_ranked(blockIdx.x, gridDim.x, nqt, 1)
+                         : xcd_remap(blockIdx.x, gridDim.x);
   const int bh = lin / nqt;
   const int qi = lin % nqt;
   const int q0 = (CAUSAL ? nqt - 1 - qi : qi) * kF8BM;
