@@ -34,6 +34,8 @@ Other modes (used to collect the rocprofv3 summaries under profiles/):
                         8-bit float forward against the plain calls (one JSON
                         line per case)
   --fp8                 the E4M3 forward alone, B=1 H=16 N=16384 d=128
+  --small               small grids: the causal B=2 H=8 N=1024 d=64 workload plain
+                        and split, and the fixed cost of a launch
   --copy-bytes BYTES    a plain device copy of BYTES bytes (counter scaling)
   --summarize DIR       turn rocprofv3 output under DIR into a text table
 """
@@ -464,6 +466,48 @@ def run_variants(args):
                           "speedup_vs_bf16": b16_ms / f8_ms}), flush=True)
 
 
+def run_small(args):
+    """Small grids: the causal bf16 B=2 H=8 N=1024 d=64 workload (64
+    workgroups of 256 rows) plain and with 2, 4, 8 key slices, and the fixed
+    cost of a launch -- bf16 B=16 H=16 non-causal at N = 64 .. 1024 (one
+    workgroup per CU up to N = 256) for d = 64 and 128 -- beside a one-element
+    torch kernel timed the same way (the floor of back-to-back launches).
+    HIP events on the current stream; one JSON line per case."""
+    import torch
+
+    import exact_attention_120_amd as fa
+    from fa_inputs import make_inputs
+
+    dev = torch.device("cuda:0")
+    B, H, N, d = 2, 8, 1024, 64
+    inp = make_inputs(B, H, N, d, "bf16", seed=0)
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    o, lse = torch.empty_like(q), torch.empty((B, H, N), device=dev)
+    sc = d ** -0.5
+    res = {"case": "small_causal", "B": B, "H": H, "N": N, "d": d,
+           "plain_us": per_call_ms(lambda: fa.fa_fwd(q, k, v, o, lse, sc, True)) * 1e3}
+    for ns in (2, 4, 8):
+        ws = torch.empty(fa.fa_fwd_splitkv_workspace_size(B, H, N, d, q.dtype, ns),
+                         dtype=torch.uint8, device=dev)
+        res[f"split{ns}_us"] = per_call_ms(
+            lambda: fa.fa_fwd_splitkv(q, k, v, o, lse, sc, True, ns, ws)) * 1e3
+    print(json.dumps(res), flush=True)
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    for dd in (64, 128):
+        for n in (64, 128, 256, 512, 1024):
+            q, k, v = (torch.randn((16, 16, n, dd), generator=g, device=dev).to(torch.bfloat16)
+                       for _ in range(3))
+            o, lse = torch.empty_like(q), torch.empty((16, 16, n), device=dev)
+            us = per_call_ms(lambda: fa.fa_fwd(q, k, v, o, lse, dd ** -0.5, False)) * 1e3
+            print(json.dumps({"case": "fixed_cost", "B": 16, "H": 16, "N": n, "d": dd,
+                              "workgroups": 256 * ((n + 255) // 256),
+                              "key_tiles_per_workgroup": (n + 63) // 64, "us": us}), flush=True)
+    x = torch.zeros(1, device=dev)
+    print(json.dumps({"case": "launch_floor", "kernel": "torch add_ on one element",
+                      "us": per_call_ms(lambda: x.add_(1.0)) * 1e3}), flush=True)
+
+
 def run_fp8(args):
     """The E4M3 forward alone at B=1 H=16 N=16384 d=128 (non-causal), timed
     like the main line; one JSON line (used for its rocprofv3 summaries)."""
@@ -576,6 +620,7 @@ def main():
     p.add_argument("--sweep-bwd", action="store_true")
     p.add_argument("--variants", action="store_true")
     p.add_argument("--fp8", action="store_true")
+    p.add_argument("--small", action="store_true")
     p.add_argument("--copy-bytes", type=int)
     p.add_argument("--summarize")
     args = p.parse_args()
@@ -596,6 +641,8 @@ def main():
         return run_variants(args)
     if args.fp8:
         return run_fp8(args)
+    if args.small:
+        return run_small(args)
     return run_main(args)
 
 
