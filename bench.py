@@ -38,6 +38,7 @@ Other modes (used to collect the rocprofv3 summaries under profiles/):
                         and split, and the fixed cost of a launch
   --copy-bytes BYTES    a plain device copy of BYTES bytes (counter scaling)
   --summarize DIR       turn rocprofv3 output under DIR into a text table
+  --summarize-by-grid DIR   kernel-trace durations per (kernel, grid size)
 """
 
 from __future__ import annotations
@@ -578,6 +579,22 @@ def _short(name: str) -> str:
     return name[:70]
 
 
+def summarize_by_grid(path):
+    """Median and minimum duration per (kernel, grid size) from the rocprofv3
+    kernel traces found under path (one row per distinct launch shape)."""
+    rows = {}
+    for f in sorted(glob.glob(os.path.join(path, "**", "*kernel_trace.csv"), recursive=True)):
+        for r in csv.DictReader(open(f)):
+            grid = r.get("Grid_Size") or r.get("Grid_Size_X") or ""
+            d = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            rows.setdefault((_short(r["Kernel_Name"]), grid), []).append(d)
+    print("| kernel | grid (threads) | dispatches | median ns | min ns |")
+    print("|---|---|---|---|---|")
+    for (k, g), v in sorted(rows.items(), key=lambda x: (x[0][0], int(x[0][1] or 0))):
+        v.sort()
+        print(f"| {k} | {g} | {len(v)} | {v[len(v) // 2]} | {v[0]} |")
+
+
 def summarize(path):
     """Print per-kernel tables from rocprofv3 CSV output found under path."""
     for f in sorted(glob.glob(os.path.join(path, "**", "*kernel_stats.csv"), recursive=True)):
@@ -623,9 +640,12 @@ def main():
     p.add_argument("--small", action="store_true")
     p.add_argument("--copy-bytes", type=int)
     p.add_argument("--summarize")
+    p.add_argument("--summarize-by-grid")
     args = p.parse_args()
     if args.summarize:
         return summarize(args.summarize)
+    if args.summarize_by_grid:
+        return summarize_by_grid(args.summarize_by_grid)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(heads shard across GPUs with no communication; see the design notes)",
