@@ -34,8 +34,9 @@ Other modes (used to collect the rocprofv3 summaries under profiles/):
                         8-bit float forward against the plain calls (one JSON
                         line per case)
   --fp8                 the E4M3 forward alone, B=1 H=16 N=16384 d=128
-  --small               small grids: the causal B=2 H=8 N=1024 d=64 workload plain
-                        and split, and the fixed cost of a launch
+  --small               small grids: the causal B=2 H=8 N=1024 d=64 workload
+                        through fa_fwd, each forward kernel and split-KV, the
+                        fixed cost of a launch and the host time of one call
   --copy-bytes BYTES    a plain device copy of BYTES bytes (counter scaling)
   --summarize DIR       turn rocprofv3 output under DIR into a text table
   --summarize-by-grid DIR   kernel-trace durations per (kernel, grid size)
@@ -469,10 +470,12 @@ def run_variants(args):
 
 def run_small(args):
     """Small grids: the causal bf16 B=2 H=8 N=1024 d=64 workload (64
-    workgroups of 256 rows) plain and with 2, 4, 8 key slices, and the fixed
-    cost of a launch -- bf16 B=16 H=16 non-causal at N = 64 .. 1024 (one
+    workgroups of 256 rows) through fa_fwd (which picks the key-split kernel
+    here), through each forward kernel alone and with 2, 4, 8 key slices; the
+    fixed cost of a launch -- bf16 B=16 H=16 non-causal at N = 64 .. 1024 (one
     workgroup per CU up to N = 256) for d = 64 and 128 -- beside a one-element
-    torch kernel timed the same way (the floor of back-to-back launches).
+    torch kernel timed the same way (the floor of back-to-back launches); and
+    the host time of one call through the binding and through the C ABI.
     HIP events on the current stream; one JSON line per case."""
     import torch
 
@@ -486,7 +489,10 @@ def run_small(args):
     o, lse = torch.empty_like(q), torch.empty((B, H, N), device=dev)
     sc = d ** -0.5
     res = {"case": "small_causal", "B": B, "H": H, "N": N, "d": d,
-           "plain_us": per_call_ms(lambda: fa.fa_fwd(q, k, v, o, lse, sc, True)) * 1e3}
+           "fa_fwd_us": per_call_ms(lambda: fa.fa_fwd(q, k, v, o, lse, sc, True)) * 1e3,
+           "key_split_us": per_call_ms(lambda: fa.fa_fwd_keysplit(q, k, v, o, lse, sc, True)) * 1e3,
+           "row_tiles_us": per_call_ms(
+               lambda: fa.fa_fwd_splitkv(q, k, v, o, lse, sc, True, 1, None)) * 1e3}
     for ns in (2, 4, 8):
         ws = torch.empty(fa.fa_fwd_splitkv_workspace_size(B, H, N, d, q.dtype, ns),
                          dtype=torch.uint8, device=dev)
@@ -507,6 +513,31 @@ def run_small(args):
     x = torch.zeros(1, device=dev)
     print(json.dumps({"case": "launch_floor", "kernel": "torch add_ on one element",
                       "us": per_call_ms(lambda: x.add_(1.0)) * 1e3}), flush=True)
+    # Host time of one call: through the Python binding, and straight through
+    # the C ABI with the arguments prepared once (B=16 H=16 N=64 d=64, one
+    # key tile per workgroup; the GPU keeps up, so these are host-bound).
+    from exact_attention_120_amd import _lib
+    q, k, v = (torch.randn((16, 16, 64, 64), generator=g, device=dev).to(torch.bfloat16)
+               for _ in range(3))
+    o, lse = torch.empty_like(q), torch.empty((16, 16, 64), device=dev)
+    lib = _lib.load()
+    raw = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), 16, 16, 64, 64,
+           0.125, 0, fa.DTYPES[q.dtype], torch.cuda.current_stream().cuda_stream)
+
+    def host_us(fn, n=4000):
+        for _ in range(100):
+            fn()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(n):
+            fn()
+        us = (time.perf_counter() - t) / n * 1e6
+        torch.cuda.synchronize()
+        return us
+    print(json.dumps({"case": "host_call", "B": 16, "H": 16, "N": 64, "d": 64,
+                      "binding_us": host_us(lambda: fa.fa_fwd(q, k, v, o, lse, 0.125, False)),
+                      "c_abi_us": host_us(lambda: lib.fa_fwd(*raw)),
+                      "torch_add_us": host_us(lambda: x.add_(1.0))}), flush=True)
 
 
 def run_fp8(args):

@@ -19,6 +19,7 @@ take Q, K, V as OCP FP8 E4M3 codes with one dequantization factor each.
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 
@@ -26,7 +27,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["FaError", "fa_fwd", "fa_bwd", "fa_fwd_ex", "fa_bwd_ex", "fa_bwd_workspace_size",
+__all__ = ["FaError", "fa_fwd", "fa_bwd", "fa_fwd_ex", "fa_fwd_keysplit", "fa_bwd_ex",
+           "fa_bwd_workspace_size",
            "fa_fwd_num_splits", "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv",
            "fa_fwd_fp8", "fa_fwd_sparse", "fa_bwd_sparse", "fa_bwd_noalloc", "fa_strerror",
            "forward",
@@ -53,18 +55,35 @@ def fa_bwd_workspace_size(B: int, H: int, N: int, d: int) -> int:
 
 
 def _check(tensors: dict, shape, dtype) -> None:
+    shape = tuple(shape)
     for name, t in tensors.items():
+        if t.dtype is dtype and t.shape == shape and t.is_cuda and t.is_contiguous():
+            continue
         if not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor")
-        if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
-            raise ValueError(f"{name}: expected contiguous {tuple(shape)} {dtype}, got "
-                             f"{tuple(t.shape)} {t.dtype} contiguous={t.is_contiguous()}")
+        raise ValueError(f"{name}: expected contiguous {shape} {dtype}, got "
+                         f"{tuple(t.shape)} {t.dtype} contiguous={t.is_contiguous()}")
+
+
+# The raw current-stream handle of a device, without building a torch Stream
+# object per call (a few microseconds saved on every call of a short kernel).
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream(t: torch.Tensor, stream) -> int:
     if stream is None:
+        if _raw_stream is not None:
+            return _raw_stream(t.get_device())
         return torch.cuda.current_stream(t.device).cuda_stream
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _on_device(t: torch.Tensor):
+    """Context that makes t's GPU current (a no-op when it already is)."""
+    idx = t.get_device()
+    if idx == torch.cuda.current_device():
+        return contextlib.nullcontext()
+    return torch.cuda.device(idx)
 
 
 def _shape(q: torch.Tensor):
@@ -80,7 +99,7 @@ def fa_fwd(q, k, v, o, lse, scale: float, causal: bool, stream=None) -> None:
     B, H, N, d = _shape(q)
     _check({"q": q, "k": k, "v": v, "o": o}, (B, H, N, d), q.dtype)
     _check({"lse": lse}, (B, H, N), torch.float32)
-    with torch.cuda.device(q.device):
+    with _on_device(q):
         st = _lib.load().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                 lse.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
                                 DTYPES[q.dtype], _stream(q, stream))
@@ -97,7 +116,7 @@ def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool, workspac
     _check({"lse": lse}, (B, H, N), torch.float32)
     if not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous GPU tensor")
-    with torch.cuda.device(q.device):
+    with _on_device(q):
         st = _lib.load().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                 do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                                 dv.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
@@ -116,7 +135,7 @@ def fa_bwd_noalloc(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool,
     _check({"q": q, "k": k, "v": v, "o": o, "do": do, "dq": dq, "dk": dk, "dv": dv},
            (B, H, N, d), q.dtype)
     _check({"lse": lse}, (B, H, N), torch.float32)
-    with torch.cuda.device(q.device):
+    with _on_device(q):
         st = _lib.load().fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                         do.data_ptr(), lse.data_ptr(), dq.data_ptr(),
                                         dk.data_ptr(), dv.data_ptr(), B, H, N, d, float(scale),
@@ -160,12 +179,30 @@ def fa_fwd_ex(q, k, v, o, lse, scale: float, causal: bool, window=None, stream=N
     _check({"k": k, "v": v}, (B, Hkv, N, d), q.dtype)
     _check({"lse": lse}, (B, H, N), torch.float32)
     opts = _options(Hkv, window)
-    with torch.cuda.device(q.device):
+    with _on_device(q):
         st = _lib.load().fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                    lse.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
                                    DTYPES[q.dtype], ctypes.byref(opts), _stream(q, stream))
     if st != _lib.FA_OK:
         raise FaError(st, "fa_fwd_ex")
+
+
+def fa_fwd_keysplit(q, k, v, o, lse, scale: float, causal: bool, window=None,
+                    stream=None) -> None:
+    """fa_fwd_ex computed by the key-split kernel (bf16/fp16), whatever the
+    shape."""
+    B, H, Hkv, N, d = _kv_shape(q, k)
+    _check({"q": q, "o": o}, (B, H, N, d), q.dtype)
+    _check({"k": k, "v": v}, (B, Hkv, N, d), q.dtype)
+    _check({"lse": lse}, (B, H, N), torch.float32)
+    opts = _options(Hkv, window)
+    with _on_device(q):
+        st = _lib.load().fa_fwd_keysplit(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                         lse.data_ptr(), B, H, N, d, float(scale),
+                                         int(bool(causal)), DTYPES[q.dtype], ctypes.byref(opts),
+                                         _stream(q, stream))
+    if st != _lib.FA_OK:
+        raise FaError(st, "fa_fwd_keysplit")
 
 
 def fa_bwd_ex(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool, workspace,
@@ -178,7 +215,7 @@ def fa_bwd_ex(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool, works
     if not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous GPU tensor")
     opts = _options(Hkv, window)
-    with torch.cuda.device(q.device):
+    with _on_device(q):
         st = _lib.load().fa_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                    do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                                    dv.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
@@ -214,7 +251,7 @@ def fa_fwd_splitkv(q, k, v, o, lse, scale: float, causal: bool, num_splits: int,
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     opts = _options(Hkv, window)
-    with torch.cuda.device(q.device):
+    with _on_device(q):
         st = _lib.load().fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                         lse.data_ptr(), B, H, N, d, float(scale),
                                         int(bool(causal)), DTYPES[q.dtype], ctypes.byref(opts),
@@ -245,7 +282,7 @@ def fa_fwd_fp8(q8, k8, v8, o, lse, scale: float, causal: bool, q_descale: float,
     _check({"o": o}, (B, H, N, d), o.dtype)
     _check({"lse": lse}, (B, H, N), torch.float32)
     opts = _options(Hkv, window)
-    with torch.cuda.device(q8.device):
+    with _on_device(q8):
         st = _lib.load().fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o.data_ptr(),
                                     lse.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
                                     float(q_descale), float(k_descale), float(v_descale),
@@ -275,7 +312,7 @@ def fa_fwd_sparse(q, k, v, o, lse, scale: float, causal: bool, block_mask, windo
     _check({"lse": lse}, (B, H, N), torch.float32)
     _check_mask(block_mask, N, q.device)
     opts = _options(Hkv, window)
-    with torch.cuda.device(q.device):
+    with _on_device(q):
         st = _lib.load().fa_fwd_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                        lse.data_ptr(), B, H, N, d, float(scale),
                                        int(bool(causal)), DTYPES[q.dtype], ctypes.byref(opts),
@@ -295,7 +332,7 @@ def fa_bwd_sparse(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool, b
     if not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous GPU tensor")
     opts = _options(Hkv, window)
-    with torch.cuda.device(q.device):
+    with _on_device(q):
         st = _lib.load().fa_bwd_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                        do.data_ptr(), lse.data_ptr(), dq.data_ptr(),
                                        dk.data_ptr(), dv.data_ptr(), B, H, N, d, float(scale),
@@ -328,15 +365,21 @@ def _default_scale(d: int, scale):
 
 
 def forward(q, k, v, causal: bool = False, scale: float | None = None, stream=None,
-            window=None, num_splits: int | None = None, block_mask=None):
+            window=None, num_splits: int | None = None, block_mask=None,
+            key_split: bool = False):
     """Allocate O and LSE with torch and run fa_fwd (fa_fwd_ex when k, v have
     fewer heads than q or a window is given; fa_fwd_splitkv, with a workspace
     allocated here, when ``num_splits`` is given; fa_fwd_sparse when
-    ``block_mask`` is given); returns (o, lse)."""
+    ``block_mask`` is given; fa_fwd_keysplit when ``key_split``); returns
+    (o, lse)."""
     B, H, N, d = _shape(q)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if block_mask is not None:
+    if key_split and (block_mask is not None or num_splits is not None):
+        raise ValueError("key_split cannot be combined with block_mask or num_splits")
+    if key_split:
+        fa_fwd_keysplit(q, k, v, o, lse, _default_scale(d, scale), causal, window, stream)
+    elif block_mask is not None:
         if num_splits is not None:
             raise ValueError("block_mask and num_splits cannot be combined")
         fa_fwd_sparse(q, k, v, o, lse, _default_scale(d, scale), causal, block_mask, window,

@@ -37,6 +37,8 @@ SIGNATURES = {
                          _opt, _vp]),
     "fa_bwd_ex": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int,
                          _flt, _int, _int, _opt, _vp, _sz, _vp]),
+    "fa_fwd_keysplit": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _flt, _int, _int,
+                               _opt, _vp]),
     "fa_fwd_num_splits": (_int, [_int, _int, _int, _int, _int]),
     "fa_fwd_splitkv_workspace_size": (_sz, [_int, _int, _int, _int, _int, _int]),
     "fa_fwd_splitkv": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _flt, _int, _int,

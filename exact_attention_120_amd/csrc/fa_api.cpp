@@ -83,12 +83,15 @@ int mask_blocks(const void* mask, int N, int dtype) {
   return nmb;
 }
 
+// key_split: 0 = the library's choice (fa_fwd, fa_fwd_ex, fa_fwd_sparse),
+// 1 = the key-split kernel (fa_fwd_keysplit; 16-bit, dense).
 int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
              int N, int d, float scale, int causal, int dtype, const fa_options* opts,
-             const void* mask, void* stream) {
+             const void* mask, void* stream, int key_split = 0) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   int st = check_shape(B, H, N, d, scale, causal, dtype);
   if (st != FA_OK) return st;
+  if (key_split && dtype == FA_F32) return FA_ERR_UNSUPPORTED;
   Opts op;
   if ((st = read_opts(opts, H, N, &op)) != FA_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
@@ -112,6 +115,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
     a.block_mask = static_cast<const uint8_t*>(mask);
     a.nmb = nmb;
   }
+  a.key_split = !mask && (key_split || fa::fwd_auto_key_split(B, H, N, d, dtype, causal));
   return hip_status(fa::launch_fwd(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -190,6 +194,12 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, 
               int N, int d, float scale, int causal, int dtype, const fa_options* opts,
               void* stream) {
   return fwd_impl(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, opts, nullptr, stream);
+}
+
+int fa_fwd_keysplit(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                    int H, int N, int d, float scale, int causal, int dtype,
+                    const fa_options* opts, void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, opts, nullptr, stream, 1);
 }
 
 int fa_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int B,

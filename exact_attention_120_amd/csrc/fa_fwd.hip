@@ -153,6 +153,96 @@ struct TileLoader {
   }
 };
 
+// One 64-key tile of a wave's 32 query rows, all three steps in order:
+// S^T = K Q^T from the stage's K tile, the online softmax (hidden scores set
+// to -inf when need_mask), O^T += V^T P^T from the stage's V tile. m is the
+// reference max the exponentials are taken against (raw scores): it moves to
+// the row max only when that max has grown by more than 2^8 in probability,
+// and O and l are rescaled with it, so O and l always share one reference.
+template <typename T, int D, bool CAUSAL>
+__device__ __forceinline__ void attend_tile(const char* stage, const int (&voff)[FwdShape<T, D>::NDT],
+                                            const typename Elem<T>::Raw (&qf)[FwdShape<T, D>::NQK],
+                                            int k0, bool need_mask, int qrow, int half, int col,
+                                            int N, float c, int wl, int wr, float& m, float& l,
+                                            f32x16 (&o)[FwdShape<T, D>::NDT]) {
+  using S = FwdShape<T, D>;
+  using E = Elem<T>;
+  using Raw = typename E::Raw;
+  constexpr int KH = S::KH;
+  // S^T = K Q^T for 64 keys x 32 queries.
+  f32x16 s[S::NMT];
+#pragma unroll
+  for (int mt = 0; mt < S::NMT; ++mt) {
+    s[mt] = f32x16{};
+    const char* kp = stage + ((mt * 32 + col) * S::KS + half * S::DH) * S::ES;
+#pragma unroll
+    for (int i = 0; i < S::NQK; ++i) s[mt] = E::mma(ld<Raw>(kp + i * KH * S::ES), qf[i], s[mt]);
+  }
+  if (need_mask) {  // diagonal, window edge or tail: hidden scores -> -inf (probability 0)
+#pragma unroll
+    for (int mt = 0; mt < S::NMT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (!key_visible(key, qrow, N, CAUSAL, wl, wr)) s[mt][r] = -INFINITY;
+      }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int mt = 0; mt < S::NMT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
+  mx = max_with_other_half(mx);
+  const float m_new = fmaxf(m, mx);
+  if (wave_any((m_new - m) * c > 8.f || m == -FLT_MAX)) {
+    const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < S::NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+  }
+  // Clamped: with no visible key yet (m = -FLT_MAX) and c > 1 the product
+  // overflows, and -inf + inf would turn hidden scores into NaN.
+  const float mc = fmaxf(m * c, -FLT_MAX);
+
+  // Probabilities -> MFMA B operands (P^T), in register order.
+  Raw pf[S::NMT * (16 / KH)];
+#pragma unroll
+  for (int mt = 0; mt < S::NMT; ++mt)
+#pragma unroll
+    for (int u = 0; u < 16 / KH; ++u) {
+      float p[KH];
+#pragma unroll
+      for (int jj = 0; jj < KH; ++jj) {
+        // c > 0 always (the host passes max(scale*log2(e), FLT_MIN)), so a
+        // hidden score (-inf) gives exactly 0.
+        p[jj] = __builtin_amdgcn_exp2f(fmaf(s[mt][u * KH + jj], c, -mc));
+      }
+      pf[mt * (16 / KH) + u] = E::pack_sum(p, l);
+    }
+
+  // O^T += V^T P^T.
+  const char* vbase = stage + S::K_BYTES;
+#pragma unroll
+  for (int dt = 0; dt < S::NDT; ++dt) {
+    const char* vp = vbase + voff[dt];
+#pragma unroll
+    for (int u = 0; u < S::NPV; ++u) {
+      Raw va;
+      if constexpr (S::TRV) {
+        const u32x2 lo = lds_read_tr16(vp + (16 * u) * D * 2);
+        const u32x2 hi = lds_read_tr16(vp + (16 * u + 8) * D * 2);
+        va = Raw{lo[0], lo[1], hi[0], hi[1]};
+      } else {
+        va = ld<Raw>(vp + u * 2 * KH * S::ES);
+      }
+      o[dt] = E::mma(va, pf[u], o[dt]);
+    }
+  }
+}
+
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(FwdArgs a) {
   using S = FwdShape<T, D>;
@@ -238,78 +328,8 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(F
   for (int dt = 0; dt < S::NDT; ++dt) o[dt] = f32x16{};
 
   auto tile = [&](const char* stage, int k0, bool need_mask) {
-    // S^T = K Q^T for 64 keys x 32 queries.
-    f32x16 s[S::NMT];
-#pragma unroll
-    for (int mt = 0; mt < S::NMT; ++mt) {
-      s[mt] = f32x16{};
-      const char* kp = stage + ((mt * 32 + col) * S::KS + half * S::DH) * S::ES;
-#pragma unroll
-      for (int i = 0; i < S::NQK; ++i) s[mt] = E::mma(ld<Raw>(kp + i * KH * S::ES), qf[i], s[mt]);
-    }
-    if (need_mask) {  // diagonal, window edge or tail: hidden scores -> -inf (probability 0)
-#pragma unroll
-      for (int mt = 0; mt < S::NMT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (!key_visible(key, qrow, N, CAUSAL, a.wl, a.wr)) s[mt][r] = -INFINITY;
-        }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < S::NMT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
-    mx = max_with_other_half(mx);
-    const float m_new = fmaxf(m, mx);
-    if (wave_any((m_new - m) * c > 8.f || m == -FLT_MAX)) {
-      const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
-      m = m_new;
-      l *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < S::NDT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-    }
-    // Clamped: with no visible key yet (m = -FLT_MAX) and c > 1 the product
-    // overflows, and -inf + inf would turn hidden scores into NaN.
-    const float mc = fmaxf(m * c, -FLT_MAX);
-
-    // Probabilities -> MFMA B operands (P^T), in register order.
-    Raw pf[S::NMT * (16 / KH)];
-#pragma unroll
-    for (int mt = 0; mt < S::NMT; ++mt)
-#pragma unroll
-      for (int u = 0; u < 16 / KH; ++u) {
-        float p[KH];
-#pragma unroll
-        for (int jj = 0; jj < KH; ++jj) {
-          // c > 0 always (the host passes max(scale*log2(e), FLT_MIN)), so
-          // a hidden score (-inf) gives exactly 0.
-          p[jj] = __builtin_amdgcn_exp2f(fmaf(s[mt][u * KH + jj], c, -mc));
-        }
-        pf[mt * (16 / KH) + u] = E::pack_sum(p, l);
-      }
-
-    // O^T += V^T P^T.
-    const char* vbase = stage + S::K_BYTES;
-#pragma unroll
-    for (int dt = 0; dt < S::NDT; ++dt) {
-      const char* vp = vbase + voff[dt];
-#pragma unroll
-      for (int u = 0; u < S::NPV; ++u) {
-        Raw va;
-        if constexpr (S::TRV) {
-          const u32x2 lo = lds_read_tr16(vp + (16 * u) * D * 2);
-          const u32x2 hi = lds_read_tr16(vp + (16 * u + 8) * D * 2);
-          va = Raw{lo[0], lo[1], hi[0], hi[1]};
-        } else {
-          va = ld<Raw>(vp + u * 2 * KH * S::ES);
-        }
-        o[dt] = E::mma(va, pf[u], o[dt]);
-      }
-    }
+    attend_tile<T, D, CAUSAL>(stage, voff, qf, k0, need_mask, qrow, half, col, N, c, a.wl, a.wr,
+                              m, l, o);
   };
 
   if (nkv == 0) {  // an empty slice: nothing to visit, an empty partial
@@ -768,6 +788,219 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a) {
   if (half == 0) L[qrow] = SPARSE && !(lt > 0.f) ? -INFINITY : m * a.scale + logf(lt);
 }
 
+// ---------------------------------------------------------------------------
+// 16-bit kernel for grids too small to fill the GPU: the key tiles of a
+// workgroup's rows are split over its waves, and the waves' partial results
+// are combined in LDS at the end -- the blockwise softmax merge within one
+// workgroup, so no float32 partials reach HBM and no second launch is needed.
+//   * 8 waves = P key parts x RG groups of 32 query rows (d = 64: 4 x 2, a
+//     workgroup of 64 rows; d = 128: 2 x 4, 128 rows). Part p takes the
+//     workgroup's key tiles p, p + P, p + 2P, ... (interleaved, so the parts
+//     stay even under the causal rule), streamed through its own pair of LDS
+//     stages by its RG waves; one workgroup barrier per step.
+//   * Each wave runs the three steps of a tile in order (attend_tile); the
+//     two waves of a SIMD overlap each other's MFMAs and softmax by
+//     themselves.
+//   * At the end the waves of parts 1 .. P-1 write their O, reference max m
+//     and sum l to LDS; the part-0 wave of each row group rescales all P
+//     partials to the largest reference and adds them (every wave holds the
+//     same (row, column) elements per lane, so the merge is elementwise).
+constexpr int kKSWaves = 8;
+constexpr int kKSThreads = kKSWaves * 64;
+
+template <int D>
+struct KSShape {
+  static constexpr int P = D == 64 ? 4 : 2;       // key parts
+  static constexpr int RG = kKSWaves / P;         // 32-row groups
+  static constexpr int BM = 32 * RG;              // query rows per workgroup
+  static constexpr int PT = RG * 64;              // threads per part
+  static constexpr int K_BYTES = kBN * (D + 8) * 2;
+  static constexpr int STAGE = K_BYTES + kBN * D * 2;
+  static constexpr int VECS = kBN * D / 8 / PT;   // 16-byte vectors per thread, per tensor
+  static constexpr int LDS_BYTES = 2 * P * STAGE;
+  static constexpr int NDT = D / 32;
+  static constexpr int MW = NDT * 16 + 2;         // words per lane of a wave's partial: O, m, l
+  static_assert(kBN * D / 8 % PT == 0, "tile must split evenly over a part");
+  static_assert(kKSWaves * MW * 64 * 4 <= LDS_BYTES, "partials fit in the stages");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(kKSThreads, 1) void fwd_ks_kernel(FwdArgs a) {
+  using S = FwdShape<T, D>;
+  using KS = KSShape<D>;
+  using E = Elem<T>;
+  using Raw = typename E::Raw;
+  constexpr int KH = S::KH;
+  static_assert(S::ES == 2 && S::STAGE == KS::STAGE && S::K_BYTES == KS::K_BYTES, "16-bit layout");
+
+  __shared__ __attribute__((aligned(16))) char lds[KS::LDS_BYTES];
+
+  const int N = a.N;
+  const int nqt = (N + KS::BM - 1) / KS::BM;
+  const int lin = CAUSAL ? xcd_remap_ranked(blockIdx.x, gridDim.x, nqt, 1)
+                         : xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = lin / nqt, qi = lin % nqt;
+  const int q0 = (CAUSAL ? nqt - 1 - qi : qi) * KS::BM;
+
+  const size_t head = (size_t)bh * N * D;
+  // Query head h attends with K/V head h / (H / Hkv).
+  const size_t kvhead = (size_t)((bh / a.H) * a.Hkv + (bh % a.H) / (a.H / a.Hkv)) * N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const HeadBuf Q(reinterpret_cast<const T*>(a.q) + head, head_bytes);
+  const HeadBuf K(reinterpret_cast<const T*>(a.k) + kvhead, head_bytes);
+  const HeadBuf V(reinterpret_cast<const T*>(a.v) + kvhead, head_bytes);
+  T* O = reinterpret_cast<T*>(a.o) + head;
+  float* L = a.lse + (size_t)bh * N;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg = wave % KS::RG, kp = wave / KS::RG;
+  const int ptid = rg * 64 + lane;     // thread index within the part
+  const int col = lane & 31, half = lane >> 5;
+  const int qw0 = q0 + 32 * rg;        // first query row of this wave
+  const int qrow = qw0 + col;          // the query row this lane serves
+  const bool wave_active = qw0 < N;
+
+  // Q^T as MFMA B operands: lane half h holds head-dim elements
+  // [h*D/2, h*D/2 + D/2) of its row, KH per MFMA.
+  Raw qf[S::NQK];
+#pragma unroll
+  for (int i = 0; i < S::NQK; ++i) qf[i] = Q.ld16((qrow * D + half * S::DH + i * KH) * 2);
+
+  // Transposing V^T operand reads (the layout of the other 16-bit kernels):
+  // lane 4r+q of 16-lane group g fetches key row 4h + r (h = g/2) and
+  // head-dim columns 32*dt + 16*(g&1) + 4q .. +4.
+  int voff[S::NDT];
+  {
+    const int g = lane >> 4, jf = lane & 15, r = jf >> 2, q = jf & 3, h = g >> 1;
+    const int b = 2 * (g & 1) + (q >> 1);
+#pragma unroll
+    for (int dt = 0; dt < S::NDT; ++dt)
+      voff[dt] = (4 * h + r) * D * 2 + (((4 * dt) ^ (b ^ v_swz<D>(r))) << 4) + (q & 1) * 8;
+  }
+
+  // Key tiles t0 .. t0+nkv-1 (those holding a key some row of the workgroup
+  // can see); this part's are t0 + kp + P*j. A wave computes on those its
+  // own rows can see.
+  const int qlast = min(q0 + KS::BM, N) - 1;
+  const int t0 = first_visible_key(q0, a.wl) / kBN;
+  const int nkv = last_visible_key(qlast, N, CAUSAL, a.wr) / kBN - t0 + 1;
+  const int wk_lo = first_visible_key(qw0, a.wl);
+  const int wk_hi = last_visible_key(min(qw0 + 31, N - 1), N, CAUSAL, a.wr);
+
+  // The part's staging: vector i of a thread is tile row idx/(D/8), columns
+  // 8*(idx % (D/8)) .. +8 with idx = ptid + PT*i (rows past N read as zeros).
+  u32x4 kr[KS::VECS], vr[KS::VECS];
+  auto load = [&](int x) {
+    const int k0 = (t0 + x) * kBN;
+#pragma unroll
+    for (int i = 0; i < KS::VECS; ++i) {
+      const int off = (k0 * D + (ptid + KS::PT * i) * 8) * 2;
+      kr[i] = K.ld16(off);
+      vr[i] = V.ld16(off);
+    }
+  };
+  auto stage_of = [&](int buf) { return lds + (kp * 2 + buf) * KS::STAGE; };
+  auto store = [&](int buf) {
+    char* Kl = stage_of(buf);
+    char* Vl = Kl + KS::K_BYTES;
+#pragma unroll
+    for (int i = 0; i < KS::VECS; ++i) {
+      const int idx = ptid + KS::PT * i;
+      const int row = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
+      st<u32x4>(Kl + (row * (D + 8) + c8) * 2, kr[i]);
+      st<u32x4>(Vl + row * D * 2 + (((c8 >> 3) ^ v_swz<D>(row)) << 4), vr[i]);
+    }
+  };
+
+  const float c = a.scale_log2;  // scale * log2(e)
+  float m = -FLT_MAX;  // reference max (raw scores)
+  float l = 0.f;       // running sum of probabilities (this lane's keys)
+  f32x16 o[S::NDT];
+#pragma unroll
+  for (int dt = 0; dt < S::NDT; ++dt) o[dt] = f32x16{};
+
+  if (kp < nkv) {
+    load(kp);
+    store(0);
+  }
+#pragma unroll
+  for (int i = 0; i < S::NQK; ++i) settle(qf[i]);
+  __syncthreads();
+
+  const int nit = (nkv + KS::P - 1) / KS::P;
+  for (int j = 0; j < nit; ++j) {
+    const int x = kp + KS::P * j, xn = x + KS::P;
+    if (xn < nkv) load(xn);
+    const int k0 = (t0 + x) * kBN;
+    if (x < nkv && wave_active && k0 <= wk_hi && k0 + kBN - 1 >= wk_lo)
+      attend_tile<T, D, CAUSAL>(stage_of(j & 1), voff, qf, k0,
+                                !block_all_visible(qw0, qw0 + 31, k0, k0 + kBN - 1, N, CAUSAL,
+                                                   a.wl, a.wr),
+                                qrow, half, col, N, c, a.wl, a.wr, m, l, o);
+    if (xn < nkv) store((j + 1) & 1);
+    __syncthreads();
+  }
+
+  // Merge the parts' partials (the stages are free: every wave passed the
+  // last barrier). Lane-major words: conflict-free writes and reads.
+  float* const part = reinterpret_cast<float*>(lds);
+  auto word = [&](int w, int i) -> float& { return part[(w * KS::MW + i) * 64 + lane]; };
+  if (kp > 0) {
+#pragma unroll
+    for (int dt = 0; dt < S::NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) word(wave, dt * 16 + r) = o[dt][r];
+    word(wave, S::NDT * 16) = m;
+    word(wave, S::NDT * 16 + 1) = l;
+  }
+  __syncthreads();
+  if (kp > 0 || !wave_active) return;
+  float mp[KS::P];
+  mp[0] = m;
+  float mmax = m;
+#pragma unroll
+  for (int p = 1; p < KS::P; ++p) {
+    mp[p] = word(rg + KS::RG * p, S::NDT * 16);
+    mmax = fmaxf(mmax, mp[p]);
+  }
+  // Rescale every partial to the largest reference (a part that saw no key
+  // of these rows has O = 0, l = 0 and m = -FLT_MAX: weight 0).
+  const float a0 = __builtin_amdgcn_exp2f(fmaxf((m - mmax) * c, -FLT_MAX));
+  l *= a0;
+#pragma unroll
+  for (int dt = 0; dt < S::NDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[dt][r] *= a0;
+#pragma unroll
+  for (int p = 1; p < KS::P; ++p) {
+    const int w = rg + KS::RG * p;
+    const float ap = __builtin_amdgcn_exp2f(fmaxf((mp[p] - mmax) * c, -FLT_MAX));
+    l += ap * word(w, S::NDT * 16 + 1);
+#pragma unroll
+    for (int dt = 0; dt < S::NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][r] += ap * word(w, dt * 16 + r);
+  }
+
+  if (qrow >= N) return;
+  const float lt = l + __shfl_xor(l, 32);
+  const float inv = 1.0f / lt;
+  T* orow = O + (size_t)qrow * D;
+#pragma unroll
+  for (int dt = 0; dt < S::NDT; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = dt * 32 + 8 * g + 4 * half;
+      const uint32_t w0 = E::bits(o[dt][4 * g] * inv) | ((uint32_t)E::bits(o[dt][4 * g + 1] * inv) << 16);
+      const uint32_t w1 = E::bits(o[dt][4 * g + 2] * inv) | ((uint32_t)E::bits(o[dt][4 * g + 3] * inv) << 16);
+      st<u32x2>(orow + d0, u32x2{w0, w1});
+    }
+  if (half == 0) L[qrow] = mmax * a.scale + logf(lt);
+}
+
 // Split-KV merge of the partials of every row: with M = max_s LSE_s and
 // w_s = exp(LSE_s - M), O = sum_s w_s O_s / sum_s w_s and
 // LSE = M + ln(sum_s w_s) -- the softmax over the union of the slices' keys,
@@ -815,11 +1048,18 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   FwdArgs args = a;
   void* kargs[] = {&args};
   const void* fn;
-  if constexpr (kPP)
+  if constexpr (kPP) {
+    if (a.key_split && a.num_splits == 1 && !a.block_mask) {
+      const int nqk = (a.N + KSShape<D>::BM - 1) / KSShape<D>::BM;
+      return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_ks_kernel<T, D, CAUSAL>),
+                             dim3((unsigned)((long long)a.B * a.H * nqk)), dim3(kKSThreads), kargs,
+                             0, stream);
+    }
     fn = a.block_mask ? reinterpret_cast<const void*>(&fwd_pp_kernel<T, D, CAUSAL, true>)
                       : reinterpret_cast<const void*>(&fwd_pp_kernel<T, D, CAUSAL, false>);
-  else
+  } else {
     fn = reinterpret_cast<const void*>(&fwd_kernel<T, D, CAUSAL>);
+  }
   hipError_t e = hipLaunchKernel(fn, grid, dim3(kPP ? kPPThreads : kThreads), kargs, 0, stream);
   if (e != hipSuccess || a.num_splits == 1) return e;
   constexpr int RPB = 256 / (D / 4);
@@ -836,7 +1076,8 @@ hipError_t dispatch_d(const FwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
-static_assert(kBM == kFwdRowsF32 && kPPBM == kFwdRows16 && kBN == kFwdKeyTile,
+static_assert(kBM == kFwdRowsF32 && kPPBM == kFwdRows16 && kBN == kFwdKeyTile &&
+                  KSShape<64>::BM == kFwdRowsKeySplitMin && KSShape<128>::BM >= kFwdRowsKeySplitMin,
               "host-side grid arithmetic (fa_host.cpp) uses these tile sizes");
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {

@@ -40,6 +40,10 @@ struct FwdArgs {
   // blocks whose scores are kept; nullptr = dense.
   const uint8_t* block_mask = nullptr;
   int nmb = 0;
+  // 16-bit inputs, dense, one slice: split the key tiles of each workgroup's
+  // rows over its waves (fwd_ks_kernel) instead of one workgroup per 256
+  // query rows.
+  bool key_split = false;
 };
 
 // Backward: forward tensors plus dO and the gradient outputs. `dsum` is the
@@ -88,8 +92,10 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 // and keys per tile.
 constexpr int kFwdRowsF32 = 128;
 constexpr int kFwdRows16 = 256;
+constexpr int kFwdRowsKeySplitMin = 64;  // the key-split kernel: 64 (d = 64) or 128 rows
 constexpr int kFwdKeyTile = 64;
 
+// Workgroups of the largest forward grid any kernel launches for a shape.
 long long fwd_grid_size(int B, int H, int N);
 
 constexpr int kMaskBlock = 64;        // block-sparse mask granularity (rows and keys)
@@ -100,5 +106,9 @@ constexpr int kMaxMaskBlocks = 1024;  // block-sparse calls: N <= 65536
 // four 64-key tiles per slice, at most 16 slices.
 int fwd_rows_per_workgroup(int dtype);
 int fwd_auto_splits(int B, int H, int N, int dtype);
+// Whether fa_fwd / fa_fwd_ex use the key-split kernel for a dense 16-bit
+// shape: when one workgroup per 256 query rows would leave compute units
+// idle, or (causal) fill them for one uneven round.
+bool fwd_auto_key_split(int B, int H, int N, int d, int dtype, int causal);
 
 }  // namespace fa

@@ -92,7 +92,10 @@ enum {
  *   stream  : hipStream_t to enqueue on.
  * One kernel: query tiles in the outer (grid) dimension, key/value tiles in
  * the inner loop, online softmax in registers; tiles above the causal
- * diagonal are never visited.
+ * diagonal are never visited. bf16/fp16 shapes with too few 256-row query
+ * tiles to give every compute unit one (B*H*ceil(N/256) < 256, or <= 256
+ * with causal = 1, where one round of tiles is uneven) run the key-split
+ * kernel of fa_fwd_keysplit instead; the results agree to float rounding.
  * Returns FA_OK or a negative status (see the conventions above).
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -193,6 +196,24 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
               const fa_options* opts, void* stream);
 
 /*
+ * fa_fwd_keysplit -- fa_fwd_ex computed by the key-split kernel, whatever
+ * the shape (fa_fwd and fa_fwd_ex choose it by themselves for small grids).
+ * A workgroup covers 64 query rows (d = 64) or 128 (d = 128); its key tiles
+ * are dealt out over 4 (d = 64) or 2 (d = 128) groups of its waves, each of
+ * which runs the online softmax over its own tiles, and the groups' partial
+ * (O, max, sum) are combined in LDS at the end: the blockwise softmax merge
+ * of the pages' sections 二.5/二.6 within one workgroup. It shortens the
+ * chain of key tiles behind each output row, for sequences whose query tiles
+ * are too few to fill the GPU, without the float32 partials and second
+ * launch of fa_fwd_splitkv. bf16 and fp16 only: FA_F32 returns
+ * FA_ERR_UNSUPPORTED. Arguments, validation and results otherwise as for
+ * fa_fwd_ex.
+ */
+int fa_fwd_keysplit(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int N, int d, float scale, int causal, int dtype,
+                    const fa_options* opts, void* stream);
+
+/*
  * fa_bwd_ex -- fa_bwd with options (``opts`` may be NULL). k, v, dk, dv are
  * [B, Hkv, N, d]; the workspace size is fa_bwd_workspace_size(B, H, N, d)
  * (it depends on the query heads only). scale, causal and opts must match
@@ -239,8 +260,10 @@ size_t fa_fwd_splitkv_workspace_size(int B, int H, int N, int d, int dtype, int 
 
 /*
  * fa_fwd_splitkv -- fa_fwd_ex computed with split-KV (see above).
- *   num_splits : 1..64 slices, or 0 for fa_fwd_num_splits' choice. With 1 it
- *                is exactly fa_fwd_ex.
+ *   num_splits : 1..64 slices, or 0 for fa_fwd_num_splits' choice. With 1
+ *                there is no split and no merge: the row-tiled kernel alone
+ *                (one workgroup per 256 query rows; 128 for FA_F32), which
+ *                is what fa_fwd_ex runs for shapes that fill the GPU.
  *   workspace  : device scratch of at least fa_fwd_splitkv_workspace_size()
  *                bytes for the same arguments, 256-byte aligned, owned by the
  *                caller; contents on entry are ignored and undefined on exit.

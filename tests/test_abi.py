@@ -28,7 +28,8 @@ def lib():
 def test_header_functions_are_exported(lib):
     names = _lib.header_functions()
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_fwd_ex", "fa_bwd_ex", "fa_bwd_workspace_size",
-                          "fa_fwd_num_splits", "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv",
+                          "fa_fwd_keysplit", "fa_fwd_num_splits",
+                          "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv",
                           "fa_fwd_fp8", "fa_fwd_sparse", "fa_bwd_sparse", "fa_bwd_noalloc",
                           "fa_strerror"}
     for n in names:
@@ -205,6 +206,29 @@ FWD_EX_CASES = [
 @pytest.mark.parametrize("kw,status", FWD_EX_CASES)
 def test_fwd_ex_rejects(lib, kw, status):
     assert fwd_ex(lib, **kw) == status
+
+
+def fwd_keysplit(lib, kv_heads=0, wl=-1, wr=-1, opts=True, q=Q, k=K, v=V, o=O, lse=LSE, B=1,
+                 H=4, N=16, d=64, causal=0, dtype=2):
+    op = ctypes.byref(_lib.FaOptions(kv_heads, wl, wr)) if opts else None
+    return lib.fa_fwd_keysplit(q, k, v, o, lse, B, H, N, d, 0.125, causal, dtype, op, None)
+
+
+# fa_fwd_keysplit validates as fa_fwd_ex does, and has no float32 kernel.
+FWD_KEYSPLIT_CASES = FWD_EX_CASES + [
+    (dict(dtype=0), FA_ERR_UNSUPPORTED),
+    (dict(dtype=0, opts=False), FA_ERR_UNSUPPORTED),
+    (dict(dtype=0, q=None), FA_ERR_INVALID_ARG),            # argument errors come first
+    (dict(dtype=0, d=96), FA_ERR_UNSUPPORTED),
+    (dict(dtype=5), FA_ERR_INVALID_ARG),
+    (dict(opts=False, o=Q), FA_ERR_INVALID_ARG),
+    (dict(N=1 << 24, d=128), FA_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("kw,status", FWD_KEYSPLIT_CASES)
+def test_fwd_keysplit_rejects(lib, kw, status):
+    assert fwd_keysplit(lib, **kw) == status
 
 
 BWD_EX_CASES = [

@@ -20,11 +20,18 @@ TOL_LSE = 1e-3
 DEV = "cuda"
 
 
-def run_fwd(inp, causal, scale):
+def run_fwd(inp, causal, scale, kernel="auto"):
+    """kernel: "auto" = fa_fwd (the library's choice), "rows" = the row-tiled
+    kernel alone (fa_fwd_splitkv with one slice), "keysplit" = fa_fwd_keysplit."""
     q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
     o = torch.full_like(q, float("nan"))  # rows never written would stay NaN
     lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=DEV)
-    fa.fa_fwd(q, k, v, o, lse, scale, causal)
+    if kernel == "rows":
+        fa.fa_fwd_splitkv(q, k, v, o, lse, scale, causal, 1, None)
+    elif kernel == "keysplit":
+        fa.fa_fwd_keysplit(q, k, v, o, lse, scale, causal)
+    else:
+        fa.fa_fwd(q, k, v, o, lse, scale, causal)
     torch.cuda.synchronize()
     return o, lse
 
@@ -49,11 +56,15 @@ def scale_of(d):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 7, 64, 129, 1000])
-def test_small_shapes_full_compare(dtype, d, causal, N):
-    print(f"\n[fwd small] dtype={dtype} d={d} causal={causal} N={N}", flush=True)
+@pytest.mark.parametrize("kernel", ["auto", "rows"])
+def test_small_shapes_full_compare(dtype, d, causal, N, kernel):
+    """Both 16-bit kernels: "auto" picks the key-split one for these grids."""
+    if dtype == "f32" and kernel != "auto":
+        pytest.skip("float32 has one forward kernel")
+    print(f"\n[fwd small] dtype={dtype} d={d} causal={causal} N={N} kernel={kernel}", flush=True)
     inp = make_inputs(2, 3, N, d, dtype, seed=N + d)
     scale = scale_of(d)
-    o, lse = run_fwd(inp, causal, scale)
+    o, lse = run_fwd(inp, causal, scale, kernel)
     ref_o, ref_l = attention_forward(to_f64(inp["q"]), to_f64(inp["k"]), to_f64(inp["v"]),
                                      scale, causal)
     check(o, lse, ref_o, ref_l, dtype)

@@ -9,7 +9,8 @@ diagonal). Rows that see no key must come back as O = 0 and LSE = -inf, and
 give zero gradients. Tolerances are those of the dense 16-bit calls: O <= 2e-2,
 LSE <= 1e-3, dQ/dK/dV <= 5e-2. With an all-ones mask the sparse kernels
 visit the same tiles in the same order as the dense ones and add only exact
-zeros besides, so their results must be bit-identical to fa_fwd_ex/fa_bwd_ex.
+zeros besides, so their results must be bit-identical to the dense row-tiled
+forward (fa_fwd_splitkv with one slice) and to fa_bwd_ex.
 """
 
 import numpy as np
@@ -188,7 +189,9 @@ def test_dense_mask_is_bit_identical(d, causal, window):
     q, k, v, do = (inp[n].to(DEV) for n in ("q", "k", "v", "do"))
     mask = make_block_mask(N, "dense").to(DEV)
     scale = scale_of(d)
-    o0, l0 = fa.forward(q, k, v, causal=causal, scale=scale, window=window)
+    # The sparse forward runs the row-tiled kernel: compare with that kernel's
+    # dense call (one split-KV slice), whatever fa_fwd_ex would pick here.
+    o0, l0 = fa.forward(q, k, v, causal=causal, scale=scale, window=window, num_splits=1)
     o1, l1 = fa.forward(q, k, v, causal=causal, scale=scale, window=window, block_mask=mask)
     assert torch.equal(o0, o1) and torch.equal(l0, l1)
     g0 = fa.backward(q, k, v, o0, do, l0, causal=causal, scale=scale, window=window)

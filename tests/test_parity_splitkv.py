@@ -92,7 +92,10 @@ def test_causal_bf16_n1k_auto_split():
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_one_slice_is_the_plain_forward_bitwise(dtype):
-    inp = make_inputs(2, 3, 500, 64, dtype, seed=43)
+    """One slice is the row-tiled kernel alone, which is what fa_fwd runs for
+    a grid of more than 256 row tiles (bf16: B=2 H=128 N=512) and for fp32."""
+    H, N = (128, 512) if dtype == "bf16" else (3, 500)
+    inp = make_inputs(2, H, N, 64, dtype, seed=43)
     q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
     for causal in (False, True):
         o0, l0 = fa.forward(q, k, v, causal=causal)

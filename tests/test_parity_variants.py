@@ -33,13 +33,27 @@ def scale_of(d):
     return float(torch.tensor(d ** -0.5, dtype=torch.float32))
 
 
-def fwd(inp, causal, scale, window):
+# Forward kernels: "auto" is fa_fwd_ex (the library's choice: the key-split
+# kernel for these small 16-bit grids), "rows" the row-tiled kernel alone
+# (fa_fwd_splitkv with one slice).
+KERNELS = ["auto", "rows"]
+
+
+def fwd(inp, causal, scale, window, kernel="auto"):
     q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
     o = torch.full_like(q, float("nan"))
     lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=DEV)
-    fa.fa_fwd_ex(q, k, v, o, lse, scale, causal, window)
+    if kernel == "rows":
+        fa.fa_fwd_splitkv(q, k, v, o, lse, scale, causal, 1, None, window)
+    else:
+        fa.fa_fwd_ex(q, k, v, o, lse, scale, causal, window)
     torch.cuda.synchronize()
     return o, lse
+
+
+def one_kernel_for_f32(dtype, kernel):
+    if dtype == "f32" and kernel != "auto":
+        pytest.skip("float32 has one forward kernel")
 
 
 def bwd(inp, causal, scale, window):
@@ -90,11 +104,14 @@ def check_bwd(got, inp, causal, scale, window, dtype):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("window", WINDOWS)
-def test_window_forward(dtype, d, causal, window):
-    print(f"\n[fwd window] dtype={dtype} d={d} causal={causal} window={window}", flush=True)
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_window_forward(dtype, d, causal, window, kernel):
+    one_kernel_for_f32(dtype, kernel)
+    print(f"\n[fwd window] dtype={dtype} d={d} causal={causal} window={window} kernel={kernel}",
+          flush=True)
     inp = make_inputs(2, 2, 300, d, dtype, seed=d + window[0] + 7 * window[1])
     scale = scale_of(d)
-    o, lse = fwd(inp, causal, scale, window)
+    o, lse = fwd(inp, causal, scale, window, kernel)
     check_fwd(o, lse, inp, causal, scale, window, dtype)
 
 
@@ -103,32 +120,37 @@ def test_window_forward(dtype, d, causal, window):
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("heads", [(4, 1), (4, 2), (6, 3)])
 @pytest.mark.parametrize("N", [129, 300])
-def test_grouped_forward(dtype, d, causal, heads, N):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_grouped_forward(dtype, d, causal, heads, N, kernel):
+    one_kernel_for_f32(dtype, kernel)
     H, Hkv = heads
-    print(f"\n[fwd grouped] dtype={dtype} d={d} causal={causal} H={H} Hkv={Hkv} N={N}",
-          flush=True)
+    print(f"\n[fwd grouped] dtype={dtype} d={d} causal={causal} H={H} Hkv={Hkv} N={N} "
+          f"kernel={kernel}", flush=True)
     inp = make_inputs(2, H, N, d, dtype, seed=N + H + Hkv, kv_heads=Hkv)
     scale = scale_of(d)
-    o, lse = fwd(inp, causal, scale, None)
+    o, lse = fwd(inp, causal, scale, None, kernel)
     check_fwd(o, lse, inp, causal, scale, None, dtype)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_grouped_window_forward_longer(dtype, causal):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_grouped_window_forward_longer(dtype, causal, kernel):
     """Windows narrower than a workgroup's rows: the key-tile range starts
     past 0 and differs between the waves of one workgroup."""
-    print(f"\n[fwd grouped window] dtype={dtype} causal={causal}", flush=True)
+    one_kernel_for_f32(dtype, kernel)
+    print(f"\n[fwd grouped window] dtype={dtype} causal={causal} kernel={kernel}", flush=True)
     inp = make_inputs(1, 4, 2000, 128, dtype, seed=21, kv_heads=2)
     scale = scale_of(128)
     for window in [(256, 0), (70, 130), (5, -1)]:
-        o, lse = fwd(inp, causal, scale, window)
+        o, lse = fwd(inp, causal, scale, window, kernel)
         check_fwd(o, lse, inp, causal, scale, window, dtype)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_window_forward_large_scale(dtype, causal):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_window_forward_large_scale(dtype, causal, kernel):
     """scale * log2(e) > 1 with a left window bound: rows whose first visited
     key tile holds none of their keys still have no reference max there
     (-FLT_MAX), whose product with the exponent multiplier overflows. The
@@ -136,11 +158,12 @@ def test_window_forward_large_scale(dtype, causal):
 
     fp32's 1e-5 is the bound at scale 1/sqrt(d); float32 score errors grow
     with the scores, so at larger scales it is multiplied by scale*sqrt(d)."""
-    print(f"\n[fwd window large scale] dtype={dtype} causal={causal}", flush=True)
+    one_kernel_for_f32(dtype, kernel)
+    print(f"\n[fwd window large scale] dtype={dtype} causal={causal} kernel={kernel}", flush=True)
     inp = make_inputs(1, 2, 700, 64, dtype, seed=23)
     for scale, window in [(1.5, (100, 0)), (4.0, (100, 40)), (1.0, (45, -1))]:
         tol = {**TOL_O, "f32": TOL_O["f32"] * max(1.0, scale * 64 ** 0.5)}
-        o, lse = fwd(inp, causal, scale, window)
+        o, lse = fwd(inp, causal, scale, window, kernel)
         check_fwd(o, lse, inp, causal, scale, window, dtype, tol_o=tol)
         q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
         o, lse = fa.forward(q, k, v, causal=causal, scale=scale, window=window, num_splits=3)
