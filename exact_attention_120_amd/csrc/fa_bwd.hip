@@ -490,7 +490,7 @@ struct IntC {
 // stage index the matrix phase re-added the stage and role offsets to each
 // of its address registers (about as many VALU instructions as MFMAs).
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool ROLE_A>
-__device__ __forceinline__ void kv16_role(const BwdArgs& a, char* lds) {
+__device__ __forceinline__ void kv16_role(const BwdArgs& a, char* lds, int bid, int nblk) {
   using S = KVShape<D>;
   using E = Elem<T>;
   using Raw = u32x4;
@@ -500,8 +500,7 @@ __device__ __forceinline__ void kv16_role(const BwdArgs& a, char* lds) {
   const int N = a.N;
   const int nkt = (N + kBN - 1) / kBN;
   const int parts = a.kv_parts;  // workgroups sharing one key tile's query heads
-  const int lin = CAUSAL ? xcd_remap_ranked(blockIdx.x, gridDim.x, nkt * parts, parts)
-                         : xcd_remap(blockIdx.x, gridDim.x);
+  const int lin = CAUSAL ? xcd_remap_ranked(bid, nblk, nkt * parts, parts) : xcd_remap(bid, nblk);
   const int bkv = lin / (nkt * parts);  // batch * Hkv + K/V head
   const int k0 = lin % (nkt * parts) / parts * kBN;
   const int part = lin % parts;
@@ -853,13 +852,19 @@ __device__ __forceinline__ void kv16_role(const BwdArgs& a, char* lds) {
   epilogue();
 }
 
+// Workgroup `bid` of `nblk` of the dK/dV grid (the XCD of bid is bid % 8).
+template <typename T, int D, bool CAUSAL, bool SPARSE>
+__device__ __forceinline__ void kv16_body(const BwdArgs& a, char* lds, int bid, int nblk) {
+  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 4)
+    kv16_role<T, D, CAUSAL, SPARSE, true>(a, lds, bid, nblk);
+  else
+    kv16_role<T, D, CAUSAL, SPARSE, false>(a, lds, bid, nblk);
+}
+
 template <typename T, int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(kKVThreads, 1) void bwd_kv16_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[SPARSE ? KVShape<D>::LDS_SPARSE : KVShape<D>::LDS];
-  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 4)
-    kv16_role<T, D, CAUSAL, SPARSE, true>(a, lds);
-  else
-    kv16_role<T, D, CAUSAL, SPARSE, false>(a, lds);
+  kv16_body<T, D, CAUSAL, SPARSE>(a, lds, blockIdx.x, gridDim.x);
 }
 
 // dK, dV = the sum of the parts' float32 partials (in part order, so the
@@ -927,22 +932,21 @@ struct DQShape {
   static constexpr int LDS_SPARSE = OFF_TL + 2 * kMaxMaskBlocks + 4 * 8;
 };
 
+// Workgroup `bid` of `nblk` of the dQ grid (the XCD of bid is bid % 8).
 template <typename T, int D, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(kDQThreads, 1) void bwd_dq16_kernel(BwdArgs a) {
+__device__ __forceinline__ void dq16_body(const BwdArgs& a, char* lds, int bid, int nblk) {
   using S = DQShape<D>;
   using E = Elem<T>;
   using Raw = u32x4;
   constexpr int ROWB = S::ROWB;
   static_assert(kMaskBlock == 2 * kDQBN && kDQBM == 4 * kMaskBlock, "mask blocks of two key tiles");
 
-  __shared__ __attribute__((aligned(16))) char lds[SPARSE ? S::LDS_SPARSE : S::LDS];
   char* const kbuf = lds;
   char* const vbuf = lds + S::NKBUF * S::TILE;
 
   const int N = a.N;
   const int nqt = (N + kDQBM - 1) / kDQBM;
-  const int lin = CAUSAL ? xcd_remap_ranked(blockIdx.x, gridDim.x, nqt, 1)
-                         : xcd_remap(blockIdx.x, gridDim.x);
+  const int lin = CAUSAL ? xcd_remap_ranked(bid, nblk, nqt, 1) : xcd_remap(bid, nblk);
   const int bh = lin / nqt;
   const int qtile = CAUSAL ? nqt - 1 - lin % nqt : lin % nqt;
   const int q0 = qtile * kDQBM;
@@ -1239,6 +1243,45 @@ __global__ __launch_bounds__(kDQThreads, 1) void bwd_dq16_kernel(BwdArgs a) {
   epilogue();
 }
 
+template <typename T, int D, bool CAUSAL, bool SPARSE>
+__global__ __launch_bounds__(kDQThreads, 1) void bwd_dq16_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[SPARSE ? DQShape<D>::LDS_SPARSE : DQShape<D>::LDS];
+  dq16_body<T, D, CAUSAL, SPARSE>(a, lds, blockIdx.x, gridDim.x);
+}
+
+// The dK/dV and dQ grids in one launch: workgroups [0, n_dq) are the dQ
+// grid, [kv0, kv0 + n_kv) the dK/dV grid (kv0 = n_dq rounded up to a
+// multiple of 8, so that both keep the XCD of each of their workgroups;
+// the workgroups in between return at once). The two kernels read the same
+// inputs and write disjoint outputs, so running them side by side changes
+// no result. What it gains: when one grid ends in a partial round -- the
+// causal dQ grid of a short sequence is a single round whose longest
+// workgroup sees every key tile and whose shortest sees one -- the other
+// grid's workgroups fill the compute units that would otherwise idle.
+template <int D, bool SPARSE>
+constexpr int fused_lds() {
+  constexpr int kv = SPARSE ? KVShape<D>::LDS_SPARSE : KVShape<D>::LDS;
+  constexpr int dq = SPARSE ? DQShape<D>::LDS_SPARSE : DQShape<D>::LDS;
+  return kv > dq ? kv : dq;
+}
+
+// Grids of at most this many workgroups (four rounds of one per compute
+// unit) are launched fused; larger ones run the two kernels one after the
+// other, where the fused launch measured the same.
+constexpr long long kFuseMaxWorkgroups = 4 * kCUs;
+
+template <typename T, int D, bool CAUSAL, bool SPARSE>
+__global__ __launch_bounds__(kKVThreads, 1) void bwd_fused16_kernel(BwdArgs a, int n_dq, int kv0,
+                                                                   int n_kv) {
+  static_assert(kKVThreads == kDQThreads, "one workgroup size");
+  __shared__ __attribute__((aligned(16))) char lds[fused_lds<D, SPARSE>()];
+  const int b = blockIdx.x;
+  if (b < n_dq)
+    dq16_body<T, D, CAUSAL, SPARSE>(a, lds, b, n_dq);
+  else if (b >= kv0)
+    kv16_body<T, D, CAUSAL, SPARSE>(a, lds, b - kv0, n_kv);
+}
+
 // D_i = sum_k dO_ik O_ik (float32) and dQ accumulator rows cleared.
 // TPR threads per row, 16 bytes of O and dO each.
 template <typename T, int D>
@@ -1309,41 +1352,55 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
       parts *= 2;
     args.kv_parts = parts;
   }
-  {
-    void* kargs[] = {&args};
-    const dim3 grid((unsigned)((long long)a.B * a.Hkv * nkt * args.kv_parts));
-    const void* fn;
-    if constexpr (sizeof(T) == 2)
-      fn = a.block_mask ? (a.causal ? reinterpret_cast<const void*>(&bwd_kv16_kernel<T, D, true, true>)
-                                    : reinterpret_cast<const void*>(&bwd_kv16_kernel<T, D, false, true>))
-                        : (a.causal ? reinterpret_cast<const void*>(&bwd_kv16_kernel<T, D, true, false>)
-                                    : reinterpret_cast<const void*>(&bwd_kv16_kernel<T, D, false, false>));
-    else
-      fn = a.causal ? reinterpret_cast<const void*>(&bwd_main_kernel<T, D, true>)
-                    : reinterpret_cast<const void*>(&bwd_main_kernel<T, D, false>);
-    hipError_t e = hipLaunchKernel(fn, grid, dim3(sizeof(T) == 2 ? kKVThreads : kThreads), kargs, 0,
-                                   stream);
-    if (e != hipSuccess) return e;
-  }
-  if constexpr (sizeof(T) == 2) if (args.kv_parts > 1) {
-    long long n4 = (long long)a.B * a.Hkv * a.N * D / 4;
-    void* kargs[] = {&args, &n4};
-    const dim3 grid((unsigned)((2 * n4 + kThreads - 1) / kThreads));
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_kvsum_kernel<T>), grid,
-                                   dim3(kThreads), kargs, 0, stream);
-    if (e != hipSuccess) return e;
-  }
   if constexpr (sizeof(T) == 2) {
-    void* kargs[] = {&args};
     const int nqt = (a.N + kDQBM - 1) / kDQBM;
-    const dim3 grid((unsigned)((long long)a.B * a.H * nqt));
-    const void* fn =
-        a.block_mask ? (a.causal ? reinterpret_cast<const void*>(&bwd_dq16_kernel<T, D, true, true>)
-                                 : reinterpret_cast<const void*>(&bwd_dq16_kernel<T, D, false, true>))
-                     : (a.causal ? reinterpret_cast<const void*>(&bwd_dq16_kernel<T, D, true, false>)
-                                 : reinterpret_cast<const void*>(&bwd_dq16_kernel<T, D, false, false>));
-    return hipLaunchKernel(fn, grid, dim3(kDQThreads), kargs, 0, stream);
+    int n_dq = (int)((long long)a.B * a.H * nqt);
+    int kv0 = (n_dq + 7) / 8 * 8;
+    int n_kv = (int)((long long)a.B * a.Hkv * nkt * args.kv_parts);
+    const bool causal = a.causal, sparse = a.block_mask != nullptr;
+    hipError_t e;
+    if ((long long)kv0 + n_kv <= kFuseMaxWorkgroups) {
+      // Short grids: dQ and dK/dV in one launch (bwd_fused16_kernel).
+      void* kargs[] = {&args, &n_dq, &kv0, &n_kv};
+      const void* fn =
+          sparse ? (causal ? reinterpret_cast<const void*>(&bwd_fused16_kernel<T, D, true, true>)
+                           : reinterpret_cast<const void*>(&bwd_fused16_kernel<T, D, false, true>))
+                 : (causal ? reinterpret_cast<const void*>(&bwd_fused16_kernel<T, D, true, false>)
+                           : reinterpret_cast<const void*>(&bwd_fused16_kernel<T, D, false, false>));
+      e = hipLaunchKernel(fn, dim3((unsigned)((long long)kv0 + n_kv)), dim3(kKVThreads), kargs, 0,
+                          stream);
+    } else {
+      // dK/dV grid, then the dQ grid (after the part sums, when there are
+      // parts; both orders give the same results).
+      void* kargs[] = {&args};
+      const void* fn =
+          sparse ? (causal ? reinterpret_cast<const void*>(&bwd_kv16_kernel<T, D, true, true>)
+                           : reinterpret_cast<const void*>(&bwd_kv16_kernel<T, D, false, true>))
+                 : (causal ? reinterpret_cast<const void*>(&bwd_kv16_kernel<T, D, true, false>)
+                           : reinterpret_cast<const void*>(&bwd_kv16_kernel<T, D, false, false>));
+      e = hipLaunchKernel(fn, dim3((unsigned)n_kv), dim3(kKVThreads), kargs, 0, stream);
+      if (e != hipSuccess) return e;
+      fn = sparse ? (causal ? reinterpret_cast<const void*>(&bwd_dq16_kernel<T, D, true, true>)
+                            : reinterpret_cast<const void*>(&bwd_dq16_kernel<T, D, false, true>))
+                  : (causal ? reinterpret_cast<const void*>(&bwd_dq16_kernel<T, D, true, false>)
+                            : reinterpret_cast<const void*>(&bwd_dq16_kernel<T, D, false, false>));
+      e = hipLaunchKernel(fn, dim3((unsigned)n_dq), dim3(kDQThreads), kargs, 0, stream);
+    }
+    if (e != hipSuccess || args.kv_parts == 1) return e;
+    long long n4 = (long long)a.B * a.Hkv * a.N * D / 4;
+    void* sargs[] = {&args, &n4};
+    const dim3 grid((unsigned)((2 * n4 + kThreads - 1) / kThreads));
+    return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_kvsum_kernel<T>), grid,
+                           dim3(kThreads), sargs, 0, stream);
   } else {
+    {
+      void* kargs[] = {&args};
+      const dim3 grid((unsigned)((long long)a.B * a.Hkv * nkt));
+      const void* fn = a.causal ? reinterpret_cast<const void*>(&bwd_main_kernel<T, D, true>)
+                                : reinterpret_cast<const void*>(&bwd_main_kernel<T, D, false>);
+      hipError_t e = hipLaunchKernel(fn, grid, dim3(kThreads), kargs, 0, stream);
+      if (e != hipSuccess) return e;
+    }
     long long n4 = rows * D / 4;
     void* kargs[] = {&args, &n4};
     const dim3 grid((unsigned)((n4 + kThreads - 1) / kThreads));
