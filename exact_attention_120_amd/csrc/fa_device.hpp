@@ -254,11 +254,14 @@ __device__ inline int last_query_seeing(int k1, int N, int wl) {
   return wl >= 0 ? min(N - 1, k1 + wl) : N - 1;
 }
 
+// MI355X: 8 XCDs (chiplets, each with its own L2) of 32 compute units.
+constexpr int kXCDs = 8, kCUsPerXCD = 32;
+
 // Workgroups are dispatched round-robin over the 8 XCDs (bid % 8). Remap so
 // that consecutive logical tiles (the query tiles of one head, which read the
 // same K/V) land on the same XCD and share its L2. A bijection on [0, total).
 __device__ inline int xcd_remap(int bid, int total) {
-  constexpr int X = 8;
+  constexpr int X = kXCDs;
   const int per = total / X, rem = total % X;
   const int x = bid % X, idx = bid / X;
   return x * per + (x < rem ? x : rem) + idx;
@@ -278,7 +281,7 @@ __device__ inline int xcd_remap(int bid, int total) {
 // with 32 heads per XCD; one head at a time lost 1-4% at N = 8192-16384).
 // Otherwise the plain remap. A bijection on [0, total) either way.
 __device__ inline int xcd_remap_ranked(int bid, int total, int per_head, int inner) {
-  constexpr int X = 8, kCUsPerXCD = 32;
+  constexpr int X = kXCDs;
   if (total % (X * per_head) != 0) return xcd_remap(bid, total);
   const int hpx = total / (X * per_head);  // heads per XCD
   int G = (kCUsPerXCD * inner + per_head - 1) / per_head;

@@ -135,3 +135,27 @@ def test_16bit_backward_is_deterministic(dtype):
     b = run(inp, True, scale_of(128), poison_workspace=False)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("window", [None, (60, 20)])
+def test_many_heads_several_rounds(window):
+    """B=1 H=256 N=512 d=64 bf16, non-causal: 512 forward and dQ workgroups
+    and 1024 dK/dV workgroups (the kernels launched one after the other, in
+    several rounds per XCD). Forward and gradients of every head against the
+    oracle."""
+    from oracle import attention_forward
+    print(f"\n[rounds] window={window}", flush=True)
+    inp = make_inputs(1, 256, 512, 64, "bf16", seed=61, backward=True)
+    q, k, v, do = (inp[n].to(DEV) for n in ("q", "k", "v", "do"))
+    scale = scale_of(64)
+    o, lse = fa.forward(q, k, v, scale=scale, window=window, num_splits=1)
+    dq, dk, dv = fa.backward(q, k, v, o, do, lse, scale=scale, window=window)
+    torch.cuda.synchronize()
+    x = [to_f64(inp[n])[0] for n in ("q", "k", "v", "do")]
+    ref_o, ref_l = attention_forward(x[0], x[1], x[2], scale, False, window=window)
+    err_o = np.abs(to_f64(o)[0] - ref_o).max()
+    err_l = np.abs(to_f64(lse)[0] - ref_l).max()
+    print(f"  fwd max errors: O {err_o:.3e}, LSE {err_l:.3e}", flush=True)
+    assert err_o <= 2e-2 and err_l <= 1e-3
+    ref = attention_backward(*x, scale, False, window=window)
+    check([to_f64(g)[0] for g in (dq, dk, dv)], ref[:3], "bf16", "rounds")
