@@ -585,8 +585,8 @@ def run_copy(args):
 
 def _short(name: str) -> str:
     """Readable kernel name from a (possibly mangled) symbol."""
-    m = re.search(r"(fwd_pp_kernel|fwd_fp8_kernel|fwd_kernel|fwd_merge_kernel|bwd_kv16_kernel|"
-                  r"bwd_kvsum_kernel|"
+    m = re.search(r"(fwd_pp_kernel|fwd_ks_kernel|fwd_fp8_kernel|fwd_kernel|fwd_merge_kernel|"
+                  r"bwd_kv16_kernel|bwd_fused16_kernel|bwd_kvsum_kernel|"
                   r"bwd_main_kernel|"
                   r"bwd_pre_kernel|bwd_dq16_kernel|bwd_dq_kernel)I(.*?)EEv", name)
     if m and m.group(1) == "fwd_fp8_kernel":  # <D, CAUSAL, output type>
