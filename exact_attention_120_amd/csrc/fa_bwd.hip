@@ -1256,8 +1256,9 @@ __global__ __launch_bounds__(kDQThreads, 1) void bwd_dq16_kernel(BwdArgs a) {
 // inputs and write disjoint outputs, so running them side by side changes
 // no result. What it gains: when one grid ends in a partial round -- the
 // causal dQ grid of a short sequence is a single round whose longest
-// workgroup sees every key tile and whose shortest sees one -- the other
-// grid's workgroups fill the compute units that would otherwise idle.
+// workgroup sees every key tile and whose shortest only those up to its own
+// rows -- the other grid's workgroups fill the compute units that would
+// otherwise idle.
 template <int D, bool SPARSE>
 constexpr int fused_lds() {
   constexpr int kv = SPARSE ? KVShape<D>::LDS_SPARSE : KVShape<D>::LDS;
