@@ -28,9 +28,9 @@ COMMON = [
 ]
 
 
-# Per-translation-unit flags. The backward kernels keep their MFMA-only
-# operands in AGPRs (pinned in the source) and want every MFMA result in
-# VGPRs, where the vector ALU reads the recomputed scores.
+# Per-translation-unit flags. The backward kernels want every MFMA result in
+# vector registers (VGPR-form MFMAs), where the vector ALU reads the
+# recomputed scores and score gradients.
 FILE_FLAGS = {
     "fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
 }
