@@ -1,6 +1,7 @@
 """Build the test-only hardware probe library (tests/hw/libfa_probe.so) for
-gfx950 with hipcc. Called by __graft_entry__.build(); the GPU test that uses
-it loads the built file and fails if it is missing."""
+gfx950 with hipcc: the FP8 matrix-instruction probe and the XCD-assignment
+probe. Called by __graft_entry__.build(); the GPU tests that use it load the
+built file and fail if it is missing."""
 
 from __future__ import annotations
 
@@ -10,7 +11,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "libfa_probe.so")
-SRC = os.path.join(HERE, "fp8_mfma_probe.hip")
+SRCS = [os.path.join(HERE, "fp8_mfma_probe.hip"), os.path.join(HERE, "xcd_probe.hip")]
 
 
 def build() -> str:
@@ -18,11 +19,11 @@ def build() -> str:
                  if c and os.path.exists(c))
     tmp = LIB + ".tmp"
     cmd = [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-x", "hip", SRC,
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-x", "hip", *SRCS,
            "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {SRC}:\n{res.stderr}")
+        raise RuntimeError(f"hipcc failed for {SRCS}:\n{res.stderr}")
     os.replace(tmp, LIB)
     return LIB
 
