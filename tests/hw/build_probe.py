@@ -1,6 +1,6 @@
 """Build the test-only hardware probe library (tests/hw/libfa_probe.so) for
-gfx950 with hipcc: the FP8 matrix-instruction probe and the XCD-assignment
-probe. Called by __graft_entry__.build(); the GPU tests that use it load the
+gfx950 with hipcc: the FP8 matrix-instruction probe, the XCD-assignment
+probe and the instruction-issue-rate probe. Called by __graft_entry__.build(); the GPU tests that use it load the
 built file and fail if it is missing."""
 
 from __future__ import annotations
@@ -11,7 +11,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "libfa_probe.so")
-SRCS = [os.path.join(HERE, "fp8_mfma_probe.hip"), os.path.join(HERE, "xcd_probe.hip")]
+SRCS = [os.path.join(HERE, f) for f in ("fp8_mfma_probe.hip", "xcd_probe.hip", "issue_probe.hip")]
 
 
 def build() -> str:

@@ -1,0 +1,88 @@
+"""Instruction issue rates on one compute unit, read from the hardware
+(tests/hw/issue_probe.hip, shader-clock cycles per wave). These rates are
+what the kernel designs rest on:
+
+* a 32x32x16 bf16 MFMA occupies a SIMD's matrix core for about 32 cycles;
+* one wave issues float32 FMAs at about half the rate of a SIMD (the
+  vector ALU finishes a wave64 instruction every 4 cycles, one wave issues
+  one every 7-9): so a softmax issued by one wave is bound by that rate;
+* a second wave on the same SIMD raises the vector rate well above one
+  wave's (measured 1.4-1.6x), which the 16-bit kernels use by pairing an
+  MFMA-phase wave with a vector-phase wave on every SIMD;
+* vector work from another wave slows an MFMA stream little.
+
+The test also reads where the waves run (HW_REG_HW_ID): waves 0-3 of a
+workgroup on four different SIMDs and wave w + 4 on the SIMD of wave w,
+which is how the 8-wave kernels get one wave of each group on every SIMD.
+It prints the table (cycles per instruction per wave) and checks the claims
+above with margins.
+"""
+
+import ctypes
+import os
+
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "hw", "libfa_probe.so")
+MFMA, FMA, EXP, IDLE = 0, 1, 2, 3
+PER_ITER = {MFMA: 8, FMA: 32, EXP: 16}
+ITERS = 20000
+
+
+def run(roles):
+    if not os.path.exists(LIB):
+        raise RuntimeError(f"{LIB} is not built (run __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB)
+    lib.fa_probe_issue.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.fa_probe_issue.restype = ctypes.c_int
+    n = len(roles)
+    cyc = torch.zeros(2 * n, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(64 * n, dtype=torch.float32, device="cuda")
+    arr = (ctypes.c_int * n)(*roles)
+    st = lib.fa_probe_issue(arr, n, ITERS, cyc.data_ptr(), sink.data_ptr(),
+                            torch.cuda.current_stream().cuda_stream)
+    assert st == 0, st
+    c = cyc.cpu().tolist()
+    simd = c[n:]
+    # The placement the kernels' wave pairing relies on: waves 0-3 on four
+    # different SIMDs, and wave w + 4 on the SIMD of wave w.
+    assert sorted(simd[:4]) == [0, 1, 2, 3], simd
+    assert all(simd[w] == simd[w - 4] for w in range(4, n)), simd
+    # Cycles per instruction of each active wave; the median over waves of a role.
+    out = {}
+    for role in (MFMA, FMA, EXP):
+        per = sorted(c[w] / (ITERS * PER_ITER[role]) for w in range(n) if roles[w] == role)
+        if per:
+            out[role] = per[len(per) // 2]
+    return out
+
+
+def test_issue_rates():
+    for _ in range(3):
+        run([MFMA] * 4 + [FMA] * 4)  # warm-up
+    rows = {
+        "1 FMA wave per SIMD": ([FMA] * 4, FMA),
+        "2 FMA waves per SIMD": ([FMA] * 8, FMA),
+        "1 exp wave per SIMD": ([EXP] * 4, EXP),
+        "1 MFMA wave per SIMD": ([MFMA] * 4, MFMA),
+        "MFMA wave + FMA wave: MFMA": ([MFMA] * 4 + [FMA] * 4, MFMA),
+        "MFMA wave + FMA wave: FMA": ([MFMA] * 4 + [FMA] * 4, FMA),
+        "MFMA wave + exp wave: MFMA": ([MFMA] * 4 + [EXP] * 4, MFMA),
+        "MFMA wave + exp wave: exp": ([MFMA] * 4 + [EXP] * 4, EXP),
+    }
+    got = {}
+    print("\n[issue rates] cycles per instruction per wave:")
+    for name, (roles, role) in rows.items():
+        got[name] = min(run(roles)[role] for _ in range(3))  # best of three
+        print(f"  {name:30s} {got[name]:6.2f}", flush=True)
+    one, two = got["1 FMA wave per SIMD"], got["2 FMA waves per SIMD"]
+    print(f"  combined rate of 2 FMA waves: {two / 2:.2f} cycles per FMA", flush=True)
+    assert 28 <= got["1 MFMA wave per SIMD"] <= 40
+    assert one >= 6.0                       # one wave: about half the SIMD's vector rate
+    assert two / 2 <= 0.8 * one             # a second wave adds at least 1.25x
+    assert got["MFMA wave + FMA wave: MFMA"] <= 1.15 * got["1 MFMA wave per SIMD"]
+    assert got["MFMA wave + exp wave: MFMA"] <= 1.15 * got["1 MFMA wave per SIMD"]
