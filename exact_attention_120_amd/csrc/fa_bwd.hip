@@ -19,6 +19,10 @@
 //   3. bwd_dq16:  queries outer (256 per workgroup), 32-key tiles inner (the
 //      forward's decomposition); S and dP are recomputed and dQ accumulates
 //      in registers, written once.
+//   Grids of at most four rounds run 2 and 3 side by side in one launch
+//   (bwd_fused16). With grouped K/V heads split over several workgroups per
+//   key tile, a fourth kernel (bwd_kvsum) adds their float32 dK/dV partials
+//   in a fixed order.
 // float32: bwd_pre (also zeroes a float32 dQ accumulator), bwd_main (keys
 // outer, dK/dV in registers, dQ added with one float32 atomic per element
 // per key tile), bwd_dq (accumulator * scale -> dQ).

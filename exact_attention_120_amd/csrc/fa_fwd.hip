@@ -11,8 +11,10 @@
 //
 // gfx950 design, 16-bit inputs (bf16, fp16): one workgroup = 8 waves = 256
 // query rows of one head, in two groups of four waves (A = waves 0-3,
-// B = waves 4-7; wave w runs on SIMD w % 4, so each SIMD holds one wave of
-// each group).
+// B = waves 4-7; waves 0-3 run on four different SIMDs and wave w + 4 on the
+// SIMD of wave w, so each SIMD holds one wave of each group).
+// For small grids, a key-split kernel (fwd_ks_kernel) deals each
+// workgroup's key tiles over its waves and merges their partials in LDS.
 //   * grid: B*H*ceil(N/256) workgroups, remapped so the query tiles of a head
 //     share one XCD's L2; causal grids run the longest rows first.
 //   * each wave owns 32 query rows; its Q tile stays in registers as MFMA B
