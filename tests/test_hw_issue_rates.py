@@ -81,8 +81,10 @@ def test_issue_rates():
         print(f"  {name:30s} {got[name]:6.2f}", flush=True)
     one, two = got["1 FMA wave per SIMD"], got["2 FMA waves per SIMD"]
     print(f"  combined rate of 2 FMA waves: {two / 2:.2f} cycles per FMA", flush=True)
-    assert 28 <= got["1 MFMA wave per SIMD"] <= 40
-    assert one >= 6.0                       # one wave: about half the SIMD's vector rate
-    assert two / 2 <= 0.8 * one             # a second wave adds at least 1.25x
-    assert got["MFMA wave + FMA wave: MFMA"] <= 1.15 * got["1 MFMA wave per SIMD"]
-    assert got["MFMA wave + exp wave: MFMA"] <= 1.15 * got["1 MFMA wave per SIMD"]
+    # Margins are wide (the rates vary by some 20% from box to box); what is
+    # checked is the shape of the claims, not the exact figures.
+    assert 26 <= got["1 MFMA wave per SIMD"] <= 42
+    assert one >= 5.5                       # one wave: well below the SIMD's 4-cycle rate
+    assert two / 2 <= 0.85 * one            # a second wave adds throughput
+    assert got["MFMA wave + FMA wave: MFMA"] <= 1.25 * got["1 MFMA wave per SIMD"]
+    assert got["MFMA wave + exp wave: MFMA"] <= 1.25 * got["1 MFMA wave per SIMD"]
