@@ -155,7 +155,8 @@ struct TileLoader {
   }
 };
 
-// One 64-key tile of a wave's 32 query rows, all three steps in order:
+// One 64-key tile of a wave's 32 query rows, all three steps in order (the
+// float32 kernel's step; 16-bit types use attend_tile16 below):
 // S^T = K Q^T from the stage's K tile, the online softmax (hidden scores set
 // to -inf when need_mask), O^T += V^T P^T from the stage's V tile. m is the
 // reference max the exponentials are taken against (raw scores): it moves to
@@ -241,6 +242,94 @@ __device__ __forceinline__ void attend_tile(const char* stage, const int (&voff)
         va = ld<Raw>(vp + u * 2 * KH * S::ES);
       }
       o[dt] = E::mma(va, pf[u], o[dt]);
+    }
+  }
+}
+
+// The same three steps for 16-bit types, with the ping-pong kernel's online
+// softmax: the exponentials are taken against the current reference m and
+// kept while no lane's sum over its 32 probabilities exceeds 2^8 (so no
+// single one does); otherwise, and while a row has no reference yet, m moves
+// to the row max, O and l are rescaled and the exponentials are taken again.
+// The row sum is a tree of float32 adds over the unrounded probabilities.
+template <typename T, int D, bool CAUSAL>
+__device__ __forceinline__ void attend_tile16(const char* stage, const int (&voff)[FwdShape<T, D>::NDT],
+                                              const typename Elem<T>::Raw (&qf)[FwdShape<T, D>::NQK],
+                                              int k0, bool need_mask, int qrow, int half, int col,
+                                              int N, float c, int wl, int wr, float& m, float& l,
+                                              f32x16 (&o)[FwdShape<T, D>::NDT]) {
+  using S = FwdShape<T, D>;
+  using E = Elem<T>;
+  using Raw = typename E::Raw;
+  constexpr int KH = S::KH;
+  static_assert(S::ES == 2 && S::NMT == 2 && KH == 8, "16-bit, 64-key tiles");
+  f32x16 s[S::NMT];
+#pragma unroll
+  for (int mt = 0; mt < S::NMT; ++mt) {
+    s[mt] = f32x16{};
+    const char* kp = stage + ((mt * 32 + col) * S::KS + half * S::DH) * S::ES;
+#pragma unroll
+    for (int i = 0; i < S::NQK; ++i) s[mt] = E::mma(ld<Raw>(kp + i * KH * S::ES), qf[i], s[mt]);
+  }
+  if (need_mask) {
+#pragma unroll
+    for (int mt = 0; mt < S::NMT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (!key_visible(key, qrow, N, CAUSAL, wl, wr)) s[mt][r] = -INFINITY;
+      }
+  }
+  float p[2 * 16];
+  float ls;
+  auto exps = [&]() {
+    const float mc = fmaxf(m * c, -FLT_MAX);
+#pragma unroll
+    for (int mt = 0; mt < S::NMT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[mt * 16 + r] = __builtin_amdgcn_exp2f(fmaf(s[mt][r], c, -mc));
+    float t[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) t[j] = p[2 * j] + p[2 * j + 1];
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+      for (int j = 0; j < w; ++j) t[j] = t[2 * j] + t[2 * j + 1];
+    ls = t[0];
+  };
+  exps();
+  if (wave_any(!(ls <= 256.f) || m == -FLT_MAX)) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < S::NMT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
+    mx = max_with_other_half(mx);
+    const float m_new = fmaxf(m, mx);
+    const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < S::NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    exps();
+  }
+  l += ls;
+  Raw pf[S::NMT * 2];
+#pragma unroll
+  for (int k = 0; k < S::NMT * 2; ++k)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) pf[k][w] = E::pack_pair(p[8 * k + 2 * w], p[8 * k + 2 * w + 1]);
+  const char* vbase = stage + S::K_BYTES;
+#pragma unroll
+  for (int dt = 0; dt < S::NDT; ++dt) {
+    const char* vp = vbase + voff[dt];
+#pragma unroll
+    for (int u = 0; u < S::NPV; ++u) {
+      const u32x2 lo = lds_read_tr16(vp + (16 * u) * D * 2);
+      const u32x2 hi = lds_read_tr16(vp + (16 * u + 8) * D * 2);
+      o[dt] = E::mma(Raw{lo[0], lo[1], hi[0], hi[1]}, pf[u], o[dt]);
     }
   }
 }
@@ -800,9 +889,9 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a) {
 //     workgroup's key tiles p, p + P, p + 2P, ... (interleaved, so the parts
 //     stay even under the causal rule), streamed through its own pair of LDS
 //     stages by its RG waves; one workgroup barrier per step.
-//   * Each wave runs the three steps of a tile in order (attend_tile); the
-//     two waves of a SIMD overlap each other's MFMAs and softmax by
-//     themselves.
+//   * Each wave runs the three steps of a tile in order (attend_tile16, with
+//     the ping-pong kernel's online softmax); the two waves of a SIMD overlap
+//     each other's MFMAs and softmax by themselves.
 //   * At the end the waves of parts 1 .. P-1 write their O, reference max m
 //     and sum l to LDS; the part-0 wave of each row group rescales all P
 //     partials to the largest reference and adds them (every wave holds the
@@ -938,7 +1027,7 @@ __global__ __launch_bounds__(kKSThreads, 1) void fwd_ks_kernel(FwdArgs a) {
     if (xn < nkv) load(xn);
     const int k0 = (t0 + x) * kBN;
     if (x < nkv && wave_active && k0 <= wk_hi && k0 + kBN - 1 >= wk_lo)
-      attend_tile<T, D, CAUSAL>(stage_of(j & 1), voff, qf, k0,
+      attend_tile16<T, D, CAUSAL>(stage_of(j & 1), voff, qf, k0,
                                 !block_all_visible(qw0, qw0 + 31, k0, k0 + kBN - 1, N, CAUSAL,
                                                    a.wl, a.wr),
                                 qrow, half, col, N, c, a.wl, a.wr, m, l, o);
