@@ -440,3 +440,24 @@ BWD_SPARSE_CASES = [
 @pytest.mark.parametrize("kw,status", BWD_SPARSE_CASES)
 def test_bwd_sparse_rejects(lib, kw, status):
     assert bwd_sparse(lib, **kw) == status
+
+
+def test_missing_library_fails_loudly():
+    """No CPU or PyTorch fallback sits behind the binding: without a built
+    library loading raises, and CPU tensors are refused before any call."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, FA_LIBRARY="/nonexistent/libfa_missing.so")
+    load = subprocess.run([sys.executable, "-c", "import exact_attention_120_amd as fa; fa._lib.load()"],
+                          cwd=root, env=env, capture_output=True, text=True, timeout=300)
+    assert load.returncode != 0
+    assert "RuntimeError" in load.stderr and "no fallback" in load.stderr, load.stderr[-2000:]
+    code = ("import torch, exact_attention_120_amd as fa\n"
+            "q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)\n"
+            "fa.fa_fwd(q, q, q, q.clone(), torch.zeros(1, 1, 64), 0.125, False)\n")
+    cpu = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
+                         timeout=300)
+    assert cpu.returncode != 0
+    assert "must be a GPU tensor" in cpu.stderr, cpu.stderr[-2000:]
